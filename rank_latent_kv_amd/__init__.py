@@ -1,3 +1,285 @@
 """MI355X-native decode attention for Multi-Head Low-Rank Attention (MLRA) and
-single-latent MLA. The compute lives in the HIP library ``libmlra.so`` (built
-in-tree); this package is its thin ctypes binding plus input generators."""
+single-latent MLA.
+
+All compute runs in the HIP library ``libmlra.so`` (built in-tree by
+``rank_latent_kv_amd.build``); this module only marshals torch tensors into the
+C ABI declared in ``include/mlra.h``. PyTorch provides device memory and the
+stream. There is no fallback: if the library is missing, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmlra.so")
+
+MLRA_OK = 0
+MLRA_ERR_INVALID_ARG = 1
+MLRA_ERR_UNSUPPORTED = 2
+MLRA_ERR_WORKSPACE = 3
+MLRA_ERR_NO_PAGES = 4
+MLRA_ERR_HIP = 5
+MLRA_BF16 = 0
+MLRA_F32 = 1
+FLAG_SEQ_LEN_CLAMPED = 1
+FLAG_BAD_PAGE = 2
+
+EXPORTED_SYMBOLS = (
+    "mlra_last_error", "mlra_version", "mlra_decode_workspace_size", "mlra_decode_validate", "mlra_decode",
+    "mla_decode", "mlra_paged_append", "mlra_paged_gather", "mlra_page_table_check", "mlra_page_pool_create",
+    "mlra_page_pool_alloc", "mlra_page_pool_free", "mlra_page_pool_num_free", "mlra_page_pool_destroy",
+)
+
+
+class MlraError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"mlra status {status}: {message}")
+        self.status = status
+
+
+class DecodeArgs(ctypes.Structure):
+    """Mirror of ``mlra_decode_args`` (include/mlra.h)."""
+    _fields_ = [
+        ("batch", ctypes.c_int32), ("num_heads", ctypes.c_int32), ("num_branches", ctypes.c_int32),
+        ("branch_dim", ctypes.c_int32), ("rope_dim", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+        ("dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
+        ("sm_scale", ctypes.c_float), ("alpha", ctypes.c_float),
+        ("q_lat", ctypes.c_void_p), ("q_rope", ctypes.c_void_p), ("kv_lat", ctypes.c_void_p),
+        ("kv_rope", ctypes.c_void_p),
+        ("row_stride", ctypes.c_int64), ("seq_stride", ctypes.c_int64),
+        ("seq_lens", ctypes.c_void_p), ("seq_lens_host", ctypes.c_void_p), ("max_seq_len", ctypes.c_int32),
+        ("page_size", ctypes.c_int32), ("page_table", ctypes.c_void_p), ("max_pages", ctypes.c_int32),
+        ("num_pages", ctypes.c_int32), ("num_splits", ctypes.c_int32),
+        ("w_v", ctypes.c_void_p), ("out", ctypes.c_void_p), ("workspace", ctypes.c_void_p),
+        ("workspace_bytes", ctypes.c_size_t), ("error_flags", ctypes.c_void_p),
+        ("event_attn_begin", ctypes.c_void_p), ("event_attn_end", ctypes.c_void_p),
+    ]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libmlra.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m rank_latent_kv_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+        P = ctypes.POINTER
+        L.mlra_last_error.restype = ctypes.c_char_p
+        L.mlra_version.restype = ctypes.c_char_p
+        L.mlra_decode_workspace_size.argtypes = [P(DecodeArgs)]
+        L.mlra_decode_workspace_size.restype = ctypes.c_size_t
+        L.mlra_decode_validate.argtypes = [P(DecodeArgs)]
+        L.mlra_decode.argtypes = [P(DecodeArgs), vp]
+        L.mla_decode.argtypes = [P(DecodeArgs), vp]
+        L.mlra_paged_append.argtypes = [vp, i64, i32, i32, i32, vp, i32, vp, vp, i32, i32, vp, vp]
+        L.mlra_paged_gather.argtypes = [vp, i64, i32, i32, i32, vp, i32, vp, i32, i32, i32, vp, vp, vp]
+        L.mlra_page_table_check.argtypes = [vp, i32, i32, vp, i32, i32]
+        L.mlra_page_pool_create.argtypes = [i32, P(vp)]
+        L.mlra_page_pool_alloc.argtypes = [vp, i32, vp]
+        L.mlra_page_pool_free.argtypes = [vp, i32, vp]
+        L.mlra_page_pool_num_free.argtypes = [vp]
+        L.mlra_page_pool_num_free.restype = i32
+        L.mlra_page_pool_destroy.argtypes = [vp]
+        L.mlra_page_pool_destroy.restype = None
+        for name in ("mlra_decode_validate", "mlra_decode", "mla_decode", "mlra_paged_append",
+                     "mlra_paged_gather", "mlra_page_table_check", "mlra_page_pool_create",
+                     "mlra_page_pool_alloc", "mlra_page_pool_free"):
+            getattr(L, name).restype = i32
+        _lib = L
+    return _lib
+
+
+def last_error() -> str:
+    return lib().mlra_last_error().decode()
+
+
+def _check(status: int):
+    if status != MLRA_OK:
+        raise MlraError(status, last_error())
+
+
+def _dtype_code(t: torch.dtype) -> int:
+    if t == torch.bfloat16:
+        return MLRA_BF16
+    if t == torch.float32:
+        return MLRA_F32
+    raise TypeError(f"unsupported dtype {t}")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _stream_handle(stream) -> Optional[int]:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def make_args(q_lat, q_rope, kv_lat, kv_rope, seq_lens, w_v, *, sm_scale: float, alpha: float,
+              row_stride: Optional[int] = None, seq_stride: Optional[int] = None,
+              max_seq_len: Optional[int] = None, seq_lens_host: Optional[torch.Tensor] = None,
+              page_table: Optional[torch.Tensor] = None, page_size: int = 64, num_pages: int = 0,
+              out: Optional[torch.Tensor] = None, out_dtype: Optional[torch.dtype] = None,
+              workspace: Optional[torch.Tensor] = None, num_splits: int = 0,
+              error_flags: Optional[torch.Tensor] = None, events=None) -> DecodeArgs:
+    """Fill ``mlra_decode_args`` from tensors (shapes as in include/mlra.h).
+
+    ``kv_lat`` / ``kv_rope`` may be views into one combined [.., rows, d_c + d_R]
+    tensor; ``row_stride`` / ``seq_stride`` default to that tensor's strides."""
+    B, H, NB, DB = q_lat.shape
+    DR = q_rope.shape[-1]
+    a = DecodeArgs()
+    a.batch, a.num_heads, a.num_branches, a.branch_dim, a.rope_dim = B, H, NB, DB, DR
+    a.head_dim = w_v.shape[1]
+    a.dtype = _dtype_code(q_lat.dtype)
+    a.out_dtype = _dtype_code(out.dtype if out is not None else (out_dtype or q_lat.dtype))
+    a.sm_scale, a.alpha = float(sm_scale), float(alpha)
+    a.q_lat, a.q_rope, a.kv_lat, a.kv_rope = _ptr(q_lat), _ptr(q_rope), _ptr(kv_lat), _ptr(kv_rope)
+    a.row_stride = int(row_stride if row_stride is not None else kv_lat.stride(-2))
+    if page_table is None:
+        a.seq_stride = int(seq_stride if seq_stride is not None else kv_lat.stride(0))
+        a.max_seq_len = int(max_seq_len if max_seq_len is not None else kv_lat.shape[-2])
+    else:
+        a.seq_stride = 0
+        a.max_seq_len = int(max_seq_len if max_seq_len is not None else page_table.shape[1] * page_size)
+        a.page_table = _ptr(page_table)
+        a.max_pages = page_table.shape[1]
+        a.page_size = page_size
+        a.num_pages = num_pages
+    a.seq_lens = _ptr(seq_lens)
+    if seq_lens_host is not None:
+        assert seq_lens_host.device.type == "cpu" and seq_lens_host.dtype == torch.int32
+        a.seq_lens_host = seq_lens_host.data_ptr()
+    a.num_splits = num_splits
+    a.w_v, a.out = _ptr(w_v), _ptr(out)
+    if workspace is not None:
+        a.workspace = workspace.data_ptr()
+        a.workspace_bytes = workspace.numel() * workspace.element_size()
+    a.error_flags = _ptr(error_flags)
+    if events is not None:
+        a.event_attn_begin, a.event_attn_end = events
+    return a
+
+
+def workspace_size(args: DecodeArgs) -> int:
+    n = lib().mlra_decode_workspace_size(ctypes.byref(args))
+    if n == 0:
+        raise MlraError(MLRA_ERR_INVALID_ARG, last_error())
+    return n
+
+
+def alloc_workspace(args: DecodeArgs, device) -> torch.Tensor:
+    n = workspace_size(args)
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def validate(args: DecodeArgs) -> int:
+    """Host-only argument check; returns the status code (0 = OK)."""
+    return lib().mlra_decode_validate(ctypes.byref(args))
+
+
+def _run(fn_name: str, q_lat, q_rope, kv_lat, kv_rope, seq_lens, w_v, *, sm_scale, alpha, out=None,
+         out_dtype=None, workspace=None, stream=None, **kw):
+    B, H, NB, DB = q_lat.shape
+    if out is None:
+        out = torch.empty((B, H, w_v.shape[1]), dtype=out_dtype or q_lat.dtype, device=q_lat.device)
+    args = make_args(q_lat, q_rope, kv_lat, kv_rope, seq_lens, w_v, sm_scale=sm_scale, alpha=alpha, out=out,
+                     workspace=workspace, **kw)
+    if workspace is None:
+        workspace = alloc_workspace(args, q_lat.device)
+        args.workspace = workspace.data_ptr()
+        args.workspace_bytes = workspace.numel()
+    _check(getattr(lib(), fn_name)(ctypes.byref(args), _stream_handle(stream)))
+    return out
+
+
+def decode(q_lat, q_rope, kv_lat, kv_rope, seq_lens, w_v, *, sm_scale: float, alpha: float, **kw) -> torch.Tensor:
+    """MLRA decode (any number of branches). Returns y [B, h, d_h]."""
+    return _run("mlra_decode", q_lat, q_rope, kv_lat, kv_rope, seq_lens, w_v, sm_scale=sm_scale, alpha=alpha, **kw)
+
+
+def mla_decode(q_lat, q_rope, kv_lat, kv_rope, seq_lens, w_v, *, sm_scale: float, alpha: float = 1.0,
+               **kw) -> torch.Tensor:
+    """Single-latent MLA decode; q_lat is [B, h, d_c] or [B, h, 1, d_c]."""
+    if q_lat.dim() == 3:
+        q_lat = q_lat.unsqueeze(2)
+    return _run("mla_decode", q_lat, q_rope, kv_lat, kv_rope, seq_lens, w_v, sm_scale=sm_scale, alpha=alpha, **kw)
+
+
+def split_rows(kv: torch.Tensor, latent_dim: int):
+    """Latent and RoPE views of a combined cache [.., rows, d_c + d_R]."""
+    return kv[..., :latent_dim], kv[..., latent_dim:]
+
+
+# ---- paged cache -------------------------------------------------------------------------
+
+def paged_append(pool: torch.Tensor, page_table: torch.Tensor, positions: torch.Tensor, rows: torch.Tensor, *,
+                 page_size: int, error_flags: Optional[torch.Tensor] = None, stream=None):
+    """pool [P, page_size, R] (or any [P*page_size, R] view), rows [B, R]."""
+    R = rows.shape[-1]
+    num_pages = pool.numel() // (page_size * pool.shape[-1])
+    _check(lib().mlra_paged_append(pool.data_ptr(), pool.stride(-2), R, page_size, num_pages, page_table.data_ptr(),
+                                   page_table.shape[1], positions.data_ptr(), rows.data_ptr(), rows.shape[0],
+                                   _dtype_code(pool.dtype), _ptr(error_flags), _stream_handle(stream)))
+
+
+def paged_gather(pool: torch.Tensor, page_table: torch.Tensor, seq_lens: torch.Tensor, max_seq_len: int, *,
+                 page_size: int, out: Optional[torch.Tensor] = None, error_flags: Optional[torch.Tensor] = None,
+                 stream=None) -> torch.Tensor:
+    R = pool.shape[-1]
+    B = page_table.shape[0]
+    if out is None:
+        out = torch.zeros((B, max_seq_len, R), dtype=pool.dtype, device=pool.device)
+    num_pages = pool.numel() // (page_size * R)
+    _check(lib().mlra_paged_gather(pool.data_ptr(), pool.stride(-2), R, page_size, num_pages, page_table.data_ptr(),
+                                   page_table.shape[1], seq_lens.data_ptr(), max_seq_len, B, _dtype_code(pool.dtype),
+                                   out.data_ptr(), _ptr(error_flags), _stream_handle(stream)))
+    return out
+
+
+def page_table_check(page_table, seq_lens, page_size: int, num_pages: int) -> None:
+    """Host check of a page table (torch int32 CPU tensors). Raises MlraError."""
+    pt = page_table.to(torch.int32).contiguous().cpu()
+    sl = seq_lens.to(torch.int32).contiguous().cpu()
+    _check(lib().mlra_page_table_check(pt.data_ptr(), pt.shape[0], pt.shape[1], sl.data_ptr(), page_size, num_pages))
+
+
+class PagePool:
+    """Deterministic host page allocator (LIFO free list) from libmlra."""
+
+    def __init__(self, num_pages: int):
+        self._h = ctypes.c_void_p()
+        _check(lib().mlra_page_pool_create(num_pages, ctypes.byref(self._h)))
+
+    def alloc(self, n: int) -> list:
+        buf = (ctypes.c_int32 * max(n, 1))()
+        _check(lib().mlra_page_pool_alloc(self._h, n, buf))
+        return list(buf[:n])
+
+    def free(self, ids: Sequence[int]) -> None:
+        buf = (ctypes.c_int32 * max(len(ids), 1))(*ids)
+        _check(lib().mlra_page_pool_free(self._h, len(ids), buf))
+
+    @property
+    def num_free(self) -> int:
+        return lib().mlra_page_pool_num_free(self._h)
+
+    def close(self):
+        if self._h:
+            lib().mlra_page_pool_destroy(self._h)
+            self._h = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

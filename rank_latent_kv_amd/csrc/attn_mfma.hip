@@ -1,0 +1,462 @@
+// Split-context flash-decode attention for MLRA / MLA on gfx950 (bf16 inputs,
+// fp32 accumulation, MFMA 32x32x16).
+//
+// One work-group (8 waves) owns one (sequence, context split). The split's
+// cache rows stream HBM -> LDS once, through a 3-stage ring filled by
+// asynchronous LDS-DMA loads, and every query head reads them from LDS: all
+// heads share one cached latent (MLRA page "原生支持张量并行的多分支低秩注意力
+// MLRA", §1.3 step 2, MQA-style attention over the latent; §3.1, each branch
+// attends over its own latent block plus the RoPE key shared by all branches).
+//
+// Work split inside the group. A "unit" is (branch b, group of 32 heads). Each
+// wave owns one branch and some head groups, and possibly only every P-th
+// 32-token sub-tile (a "phase"); phases are merged in LDS at the end.
+//
+// Per 32-token sub-tile and unit:
+//   scores  S^T[tok x head] = C_ext[tok x (d_R+d_b)] . Q_ext^T, MFMA with the
+//           exact bf16 query and fp32 accumulation; the logit in log2 units is
+//           x = S * tau*log2(e) (one fma that also subtracts the reference max);
+//   softmax lazy running max: the reference m only moves when a logit exceeds it
+//           by more than kRescaleThreshold (then O and l are rescaled); p = 2^(x-m),
+//           packed to bf16; l accumulates the packed p with a bf16 dot2 so the
+//           normaliser sums exactly the weights the P.C product uses;
+//   values  O^T[feat x head] += C_b^T[feat x tok] . P^T[tok x head], MFMA, with
+//           the transposed latent read by ds_read_b64_tr_b16.
+// Each split writes its unnormalised (o, m, l); the merge kernel combines the
+// splits (log-sum-exp) and applies W^V per branch.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+
+#include "mlra_internal.h"
+
+namespace mlra {
+namespace {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f32x2;
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4;
+typedef __attribute__((address_space(3))) char lds_char;
+typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+constexpr int kWaves = 8;
+constexpr int kThreads = kWaves * 64;
+constexpr int kStages = 3;
+constexpr int kPageCache = 256;            // page ids of one split kept in LDS
+constexpr float kRescaleThreshold = 8.0f;  // log2 units: p = 2^x stays <= 256
+
+template <int NB, int DB, int DR, int HEADS>
+struct Cfg {
+  static constexpr int NHG = (HEADS + 31) / 32;          // head groups (MFMA N = 32)
+  static constexpr int WPB = kWaves / NB;                // waves per branch
+  static constexpr int HGSPLIT = WPB < NHG ? WPB : NHG;  // head-group slots per branch
+  static constexpr int HPW = NHG / HGSPLIT;              // head groups per wave
+  static constexpr int P = WPB / HGSPLIT;                // token phases
+  static constexpr int SUB = P > 4 ? P : 4;              // 32-token sub-tiles per stage
+  static constexpr int ST = 32 * SUB;                    // tokens per stage
+  static constexpr int NCL = NB * DB / 8;                // latent 16-byte chunks per row
+  static constexpr int NCR = DR / 8;                     // RoPE 16-byte chunks per row
+  static constexpr int NCH = NCL + NCR;
+  static constexpr int SUB_BYTES = 32 * NCH * 16;
+  static constexpr int STAGE_BYTES = ST * NCH * 16;
+  static constexpr int DMA_PER_STAGE = ST * NCH / 64;    // wave-wide 1 KiB DMA instructions
+  static constexpr int DMA_PER_WAVE = DMA_PER_STAGE / kWaves;
+  static constexpr int MT = DB / 32;                     // value M-tiles (32 features)
+  static constexpr int KR = DR / 16;                     // RoPE K-chunks of the score
+  static constexpr int KL = DB / 16;                     // latent K-chunks of the score
+  static constexpr int MERGE_WAVES = kWaves - NB * HGSPLIT;
+  static constexpr int MERGE_FLOATS = HPW * (16 * MT + 2) * 64;   // per wave record
+  static constexpr int RING_BYTES = kStages * STAGE_BYTES;
+  static constexpr int MERGE_BYTES = MERGE_WAVES * MERGE_FLOATS * 4;
+  static constexpr int LDS_BYTES = (RING_BYTES > MERGE_BYTES ? RING_BYTES : MERGE_BYTES) + kPageCache * 4;
+  static_assert(kWaves % NB == 0, "branches must divide the waves");
+  static_assert(NHG % HGSPLIT == 0, "head groups must split evenly");
+  static_assert(SUB % P == 0, "phases must divide the sub-tiles");
+  static_assert(DMA_PER_STAGE % kWaves == 0, "stage DMA must split evenly over waves");
+  static_assert(DB % 32 == 0 && DR % 16 == 0, "MFMA tiling");
+  static_assert(NCH % 8 == 0 || NCH % 8 == 4, "chunk rotation assumes NCH = 0 or 4 mod 8");
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+};
+
+// Rotation of the 16-byte chunk positions of token t inside its LDS row, so that
+// eight consecutive tokens reading the same chunk hit eight different bank groups.
+template <int NCH>
+__device__ __forceinline__ int chunk_rot(int t) {
+  if constexpr (NCH % 8 == 0) return t & 7;
+  else return (t & 7) >> 1;
+}
+
+template <int NCH>
+__device__ __forceinline__ int lds_chunk_offset(int t, int c) {
+  int pos = c + chunk_rot<NCH>(t);
+  if (pos >= NCH) pos -= NCH;
+  return (t * NCH + pos) * 16;
+}
+
+// 16 bytes per lane from global memory straight into LDS at m0 + 16*lane.
+// Issued through asm so that the compiler does not add a conservative wait for
+// the whole queue before LDS reads; the kernel waits on vmcnt itself.
+__device__ __forceinline__ void dma16(const void* gaddr, uint32_t lds_addr) {
+  asm volatile(
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %0, off"
+      :
+      : "v"(gaddr), "s"(lds_addr)
+      : "memory", "m0");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+
+__device__ __forceinline__ void block_barrier() { asm volatile("s_barrier" : : : "memory"); }
+
+__device__ __forceinline__ float other_half(float x) {
+  // value held by lane l ^ 32 (the lane holding the other 16 tokens of a head)
+  return __shfl_xor(x, 32, 64);
+}
+
+__device__ __forceinline__ bf16x8 load_q8(const __bf16* src) {
+  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(src));
+}
+
+template <int NB, int DB, int DR, int HEADS, bool PAGED>
+__global__ __launch_bounds__(kThreads, 1) void attn_mfma_kernel(AttnParams p) {
+  using C = Cfg<NB, DB, DR, HEADS>;
+  __shared__ __attribute__((aligned(1024))) char smem[C::LDS_BYTES];
+  int* ptab = reinterpret_cast<int*>(smem + C::LDS_BYTES - kPageCache * 4);
+
+  const int beta = blockIdx.y;
+  const int split = blockIdx.x;
+  int L = p.seq_lens[beta];
+  if (L < 1 || L > p.max_seq_len) {
+    if (threadIdx.x == 0 && split == 0 && p.error_flags) atomicOr(p.error_flags, 1u);
+    L = L < 0 ? 0 : (L > p.max_seq_len ? p.max_seq_len : L);
+  }
+  const int t0 = split * p.split_tokens;
+  if (t0 >= L) return;
+  const int t1 = min(L, t0 + p.split_tokens);
+  const int nst = (t1 - t0 + C::ST - 1) / C::ST;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int b = wave / C::WPB;
+  const int wr = wave % C::WPB;
+  const int hgslot = wr % C::HGSPLIT;
+  const int phase = wr / C::HGSPLIT;
+  const int g = lane >> 5;          // lane half
+  const int n32 = lane & 31;        // head within a group / token within a sub-tile
+
+  // ---- paged: this split's page ids into LDS -------------------------------------------
+  int first_page = 0;
+  if constexpr (PAGED) {
+    first_page = t0 >> p.page_shift;
+    const int last_page = (t1 - 1) >> p.page_shift;
+    for (int i = tid; i <= last_page - first_page; i += kThreads) {
+      int pg = p.page_table[(int64_t)beta * p.max_pages + first_page + i];
+      if (pg < 0 || pg >= p.num_pages) {
+        if (p.error_flags) atomicOr(p.error_flags, 2u);
+        pg = 0;
+      }
+      ptab[i] = pg;
+    }
+    __syncthreads();
+  }
+
+  // ---- DMA lane plan (stage-invariant) --------------------------------------------------
+  int dtok[C::DMA_PER_WAVE];
+  uint32_t dsrc[C::DMA_PER_WAVE];
+  bool drope[C::DMA_PER_WAVE];
+#pragma unroll
+  for (int i = 0; i < C::DMA_PER_WAVE; ++i) {
+    const int f = (wave + kWaves * i) * 64 + lane;
+    const int t = f / C::NCH;
+    const int pos = f - t * C::NCH;
+    int c = pos - chunk_rot<C::NCH>(t);
+    if (c < 0) c += C::NCH;
+    dtok[i] = t;
+    drope[i] = c >= C::NCL;
+    dsrc[i] = drope[i] ? (uint32_t)(c - C::NCL) * 16u : (uint32_t)c * 16u;
+  }
+  const uint32_t smem_lds = (uint32_t)(uintptr_t)(lds_char*)(smem);
+  const char* seq_lat = p.kv_lat + (PAGED ? 0 : (int64_t)beta * p.seq_stride_b);
+  const char* seq_rope = p.kv_rope + (PAGED ? 0 : (int64_t)beta * p.seq_stride_b);
+
+  auto issue_stage = [&](int s) {
+    const int tok0 = t0 + s * C::ST;
+    const bool tail = tok0 + C::ST > t1;
+    const uint32_t ring = smem_lds + (uint32_t)((s % kStages) * C::STAGE_BYTES);
+#pragma unroll
+    for (int i = 0; i < C::DMA_PER_WAVE; ++i) {
+      int tok = tok0 + dtok[i];
+      if (tail) tok = min(tok, t1 - 1);
+      int64_t row;
+      if constexpr (PAGED) {
+        const int pg = ptab[(tok >> p.page_shift) - first_page];
+        row = ((int64_t)pg << p.page_shift) | (tok & ((1 << p.page_shift) - 1));
+      } else {
+        row = tok;
+      }
+      const char* src = (drope[i] ? seq_rope : seq_lat) + row * p.row_stride_b + dsrc[i];
+      dma16(src, __builtin_amdgcn_readfirstlane(ring + (uint32_t)((wave + kWaves * i) * 1024)));
+    }
+  };
+
+  // ---- queries: B operands (exact bf16 values) ---------------------------------------------
+  bf16x8 qr[C::HPW][C::KR];
+  bf16x8 ql[C::HPW][C::KL];
+#pragma unroll
+  for (int h = 0; h < C::HPW; ++h) {
+    const int head = (hgslot * C::HPW + h) * 32 + n32;
+    const bool live = head < p.H;
+    const __bf16* qrp = reinterpret_cast<const __bf16*>(p.q_rope) + ((int64_t)beta * p.H + head) * DR;
+    const __bf16* qlp =
+        reinterpret_cast<const __bf16*>(p.q_lat) + (((int64_t)beta * p.H + head) * NB + b) * DB;
+#pragma unroll
+    for (int k = 0; k < C::KR; ++k) qr[h][k] = live ? load_q8(qrp + 16 * k + 8 * g) : bf16x8{};
+#pragma unroll
+    for (int k = 0; k < C::KL; ++k) ql[h][k] = live ? load_q8(qlp + 16 * k + 8 * g) : bf16x8{};
+  }
+
+  // ---- per-lane LDS offsets inside a sub-tile -------------------------------------------
+  int off_r[C::KR], off_l[C::KL], off_v[C::MT];
+#pragma unroll
+  for (int k = 0; k < C::KR; ++k) off_r[k] = lds_chunk_offset<C::NCH>(n32, C::NCL + 2 * k + g);
+#pragma unroll
+  for (int k = 0; k < C::KL; ++k) off_l[k] = lds_chunk_offset<C::NCH>(n32, b * (DB / 8) + 2 * k + g);
+  {
+    const int q4 = lane >> 4, jj = lane & 15;
+    const int tt = 4 * (q4 >> 1) + (jj >> 2);                       // token within a 8-token slab
+#pragma unroll
+    for (int mt = 0; mt < C::MT; ++mt) {
+      const int f = b * DB + 32 * mt + 16 * (q4 & 1) + 4 * (jj & 3); // feature of this lane's 8-byte word
+      off_v[mt] = lds_chunk_offset<C::NCH>(tt, f >> 3) + (f & 7) * 2;
+    }
+  }
+
+  // ---- running state ---------------------------------------------------------------------
+  f32x16 acc[C::HPW][C::MT];
+  float mref[C::HPW], lsum[C::HPW];
+  bool started[C::HPW];
+  const float qs = p.q_scale;       // tau * log2(e) > 0
+#pragma unroll
+  for (int h = 0; h < C::HPW; ++h) {
+#pragma unroll
+    for (int mt = 0; mt < C::MT; ++mt) acc[h][mt] = f32x16{};
+    mref[h] = -INFINITY;
+    lsum[h] = 0.f;
+    started[h] = false;
+  }
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+
+  // ---- main loop ---------------------------------------------------------------------------
+  issue_stage(0);
+  if (nst > 1) issue_stage(1);
+  for (int s = 0; s < nst; ++s) {
+    if (s + 1 < nst) wait_vmcnt<C::DMA_PER_WAVE>();
+    else wait_vmcnt<0>();
+    block_barrier();
+    if (s + 2 < nst) issue_stage(s + 2);
+
+    const int stage_tok0 = t0 + s * C::ST;
+    const lds_char* stage = (const lds_char*)smem + (s % kStages) * C::STAGE_BYTES;
+#pragma unroll
+    for (int u = 0; u < C::SUB; ++u) {
+      if (u % C::P != phase) continue;
+      const int valid = t1 - (stage_tok0 + 32 * u);
+      if (valid <= 0) continue;
+      const lds_char* sub = stage + u * C::SUB_BYTES;
+
+      bf16x8 ar[C::KR], al[C::KL];
+#pragma unroll
+      for (int k = 0; k < C::KR; ++k) ar[k] = *(const lds_bf16x8*)(sub + off_r[k]);
+#pragma unroll
+      for (int k = 0; k < C::KL; ++k) al[k] = *(const lds_bf16x8*)(sub + off_l[k]);
+
+      f32x16 sc[C::HPW];
+#pragma unroll
+      for (int h = 0; h < C::HPW; ++h) {
+        sc[h] = f32x16{};
+#pragma unroll
+        for (int k = 0; k < C::KR; ++k) sc[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ar[k], qr[h][k], sc[h], 0, 0, 0);
+#pragma unroll
+        for (int k = 0; k < C::KL; ++k) sc[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al[k], ql[h][k], sc[h], 0, 0, 0);
+      }
+
+      // transposed latent block for P.C: [feature x token], two 4-token halves per K-chunk
+      bf16x8 av[2][C::MT];
+#pragma unroll
+      for (int kc = 0; kc < 2; ++kc) {
+#pragma unroll
+        for (int mt = 0; mt < C::MT; ++mt) {
+          const lds_char* a0 = sub + off_v[mt] + (16 * kc) * C::NCH * 16;
+          const lds_char* a1 = a0 + 8 * C::NCH * 16;
+          s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(a0));
+          s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(a1));
+          bf16x4 blo = __builtin_bit_cast(bf16x4, lo), bhi = __builtin_bit_cast(bf16x4, hi);
+          av[kc][mt] = bf16x8{blo[0], blo[1], blo[2], blo[3], bhi[0], bhi[1], bhi[2], bhi[3]};
+        }
+      }
+
+#pragma unroll
+      for (int h = 0; h < C::HPW; ++h) {
+        f32x16& x = sc[h];
+        if (valid < 32) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int tok = 8 * (r >> 2) + 4 * g + (r & 3);
+            if (tok >= valid) x[r] = -INFINITY;
+          }
+        }
+        float mx = x[0];            // raw units (scale > 0 keeps the order)
+#pragma unroll
+        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, x[r]);
+        if (!started[h]) {
+          mref[h] = fmaxf(mx, other_half(mx)) * qs;
+          started[h] = true;
+        } else {
+          const float xm = fmaf(mx, qs, -mref[h]);
+          if (__builtin_amdgcn_ballot_w64(xm > kRescaleThreshold) != 0) {
+            const float d = fmaxf(fmaxf(xm, other_half(xm)), 0.f);
+            const float f = __builtin_amdgcn_exp2f(-d);
+            mref[h] += d;
+            lsum[h] *= f;
+#pragma unroll
+            for (int mt = 0; mt < C::MT; ++mt) acc[h][mt] *= f;
+          }
+        }
+        const float negm = -mref[h];
+        bf16x2 pk[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          f32x2 e = {__builtin_amdgcn_exp2f(fmaf(x[2 * k], qs, negm)), __builtin_amdgcn_exp2f(fmaf(x[2 * k + 1], qs, negm))};
+          pk[k] = __builtin_convertvector(e, bf16x2);
+          lsum[h] = __builtin_amdgcn_fdot2_f32_bf16(pk[k], ones, lsum[h], false);
+        }
+#pragma unroll
+        for (int kc = 0; kc < 2; ++kc) {
+          bf16x8 pb = {pk[4 * kc][0], pk[4 * kc][1], pk[4 * kc + 1][0], pk[4 * kc + 1][1],
+                       pk[4 * kc + 2][0], pk[4 * kc + 2][1], pk[4 * kc + 3][0], pk[4 * kc + 3][1]};
+#pragma unroll
+          for (int mt = 0; mt < C::MT; ++mt)
+            acc[h][mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[kc][mt], pb, acc[h][mt], 0, 0, 0);
+        }
+      }
+    }
+  }
+
+  // ---- combine halves, merge phases, write this split's partial state -----------------------
+#pragma unroll
+  for (int h = 0; h < C::HPW; ++h) lsum[h] += other_half(lsum[h]);
+
+  if constexpr (C::P > 1) {
+    block_barrier();   // every wave is done with the ring; reuse it for the merge records
+    float* rec = reinterpret_cast<float*>(smem);
+    if (phase > 0) {
+      const int slot = b * (C::WPB - C::HGSPLIT) + (phase - 1) * C::HGSPLIT + hgslot;
+      float* dst = rec + slot * C::MERGE_FLOATS;
+#pragma unroll
+      for (int h = 0; h < C::HPW; ++h) {
+        float* d = dst + h * (16 * C::MT + 2) * 64;
+#pragma unroll
+        for (int mt = 0; mt < C::MT; ++mt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) d[(16 * mt + r) * 64 + lane] = acc[h][mt][r];
+        d[(16 * C::MT) * 64 + lane] = mref[h];
+        d[(16 * C::MT + 1) * 64 + lane] = lsum[h];
+      }
+    }
+    __syncthreads();
+    if (phase > 0) return;
+#pragma unroll
+    for (int h = 0; h < C::HPW; ++h) {
+      float mstar = mref[h];
+      for (int q = 1; q < C::P; ++q) {
+        const float* d = rec + (b * (C::WPB - C::HGSPLIT) + (q - 1) * C::HGSPLIT + hgslot) * C::MERGE_FLOATS +
+                         h * (16 * C::MT + 2) * 64;
+        mstar = fmaxf(mstar, d[(16 * C::MT) * 64 + lane]);
+      }
+      const float f0 = __builtin_amdgcn_exp2f(mref[h] - mstar);
+      float l = lsum[h] * f0;
+#pragma unroll
+      for (int mt = 0; mt < C::MT; ++mt) acc[h][mt] *= f0;
+      for (int q = 1; q < C::P; ++q) {
+        const float* d = rec + (b * (C::WPB - C::HGSPLIT) + (q - 1) * C::HGSPLIT + hgslot) * C::MERGE_FLOATS +
+                         h * (16 * C::MT + 2) * 64;
+        const float fq = __builtin_amdgcn_exp2f(d[(16 * C::MT) * 64 + lane] - mstar);
+        l += d[(16 * C::MT + 1) * 64 + lane] * fq;
+#pragma unroll
+        for (int mt = 0; mt < C::MT; ++mt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[h][mt][r] += d[(16 * mt + r) * 64 + lane] * fq;
+      }
+      mref[h] = mstar;
+      lsum[h] = l;
+    }
+  }
+
+#pragma unroll
+  for (int h = 0; h < C::HPW; ++h) {
+    const int head = (hgslot * C::HPW + h) * 32 + n32;
+    if (head >= p.H) continue;
+    const int64_t rec = (((int64_t)beta * p.num_splits + split) * p.H + head) * NB + b;
+    float* o = p.ws_o + rec * DB;
+#pragma unroll
+    for (int mt = 0; mt < C::MT; ++mt)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        float4 v = make_float4(acc[h][mt][4 * q4], acc[h][mt][4 * q4 + 1], acc[h][mt][4 * q4 + 2], acc[h][mt][4 * q4 + 3]);
+        *reinterpret_cast<float4*>(o + 32 * mt + 8 * q4 + 4 * g) = v;
+      }
+    if (g == 0) {
+      p.ws_ml[rec * 2] = mref[h];
+      p.ws_ml[rec * 2 + 1] = lsum[h];
+    }
+  }
+}
+
+template <int NB, int DB, int DR, int HEADS>
+hipError_t launch_shape(const AttnParams& p, bool paged, int grid_splits, hipStream_t stream) {
+  dim3 grid(grid_splits, p.B);
+  if (paged)
+    hipLaunchKernelGGL((attn_mfma_kernel<NB, DB, DR, HEADS, true>), grid, dim3(kThreads), 0, stream, p);
+  else
+    hipLaunchKernelGGL((attn_mfma_kernel<NB, DB, DR, HEADS, false>), grid, dim3(kThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+// Shapes built with the MFMA path: (branches, branch width, RoPE width, heads).
+#define MLRA_MFMA_SHAPES(X) \
+  X(4, 32, 32, 64)          \
+  X(1, 128, 32, 64)         \
+  X(1, 32, 32, 16)          \
+  X(1, 32, 32, 64)          \
+  X(2, 64, 32, 64)
+
+int mfma_stage_tokens(int nb, int db, int dr, int heads) {
+#define X(xNB, xDB, xDR, xH) \
+  if (nb == xNB && db == xDB && dr == xDR && heads == xH) return Cfg<xNB, xDB, xDR, xH>::ST;
+  MLRA_MFMA_SHAPES(X)
+#undef X
+  return 0;
+}
+
+hipError_t launch_attn_mfma(const AttnParams& p, bool paged, int grid_splits, hipStream_t stream) {
+#define X(xNB, xDB, xDR, xH) \
+  if (p.NB == xNB && p.DB == xDB && p.DR == xDR && p.H == xH) return launch_shape<xNB, xDB, xDR, xH>(p, paged, grid_splits, stream);
+  MLRA_MFMA_SHAPES(X)
+#undef X
+  return hipErrorInvalidValue;
+}
+
+}  // namespace mlra

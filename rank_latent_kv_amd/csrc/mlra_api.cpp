@@ -1,0 +1,400 @@
+// Host side of libmlra.so: argument validation (no HIP calls), launch planning,
+// the page allocator, and the exported C ABI declared in include/mlra.h.
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include <hip/hip_runtime_api.h>
+
+#include "mlra.h"
+#include "mlra_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+mlra_status fail(mlra_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+mlra_status ok() {
+  g_last_error.clear();
+  return MLRA_OK;
+}
+
+bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
+int ilog2(int x) {
+  int s = 0;
+  while ((1 << s) < x) ++s;
+  return s;
+}
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Work-groups the automatic split count aims for: one per compute unit of an
+// MI355X (256 CUs; the MFMA kernel keeps one 8-wave group per CU).
+constexpr int64_t kTargetGroups = 256;
+constexpr int kMaxSplits = 4096;
+constexpr int kPageCache = 256;
+
+struct Plan {
+  bool mfma = false;
+  bool paged = false;
+  int stage = 0;          // split granularity in tokens
+  int split_tokens = 0;
+  int num_splits = 0;
+  size_t ws_o_bytes = 0;
+  size_t ws_ml_bytes = 0;
+  size_t ws_bytes = 0;
+};
+
+int64_t total_tokens_estimate(const mlra_decode_args* a) {
+  if (a->seq_lens_host) {
+    int64_t t = 0;
+    for (int i = 0; i < a->batch; ++i) t += std::min(std::max(a->seq_lens_host[i], 0), a->max_seq_len);
+    return std::max<int64_t>(t, 1);
+  }
+  return (int64_t)a->batch * a->max_seq_len;
+}
+
+// Validate the arguments and decide the launch. Pure host code: no HIP calls.
+mlra_status make_plan(const mlra_decode_args* a, bool check_pointers, Plan* plan) {
+  if (!a) return fail(MLRA_ERR_INVALID_ARG, "args is NULL");
+  if (a->batch < 1) return fail(MLRA_ERR_INVALID_ARG, "batch must be >= 1 (got %d)", a->batch);
+  if (a->num_heads < 1) return fail(MLRA_ERR_INVALID_ARG, "num_heads must be >= 1 (got %d)", a->num_heads);
+  if (a->num_branches < 1) return fail(MLRA_ERR_INVALID_ARG, "num_branches must be >= 1 (got %d)", a->num_branches);
+  if (a->branch_dim < 1) return fail(MLRA_ERR_INVALID_ARG, "branch_dim must be >= 1 (got %d)", a->branch_dim);
+  if (a->rope_dim < 0) return fail(MLRA_ERR_INVALID_ARG, "rope_dim must be >= 0 (got %d)", a->rope_dim);
+  if (a->head_dim < 1) return fail(MLRA_ERR_INVALID_ARG, "head_dim must be >= 1 (got %d)", a->head_dim);
+  if (a->dtype != MLRA_BF16 && a->dtype != MLRA_F32) return fail(MLRA_ERR_INVALID_ARG, "dtype %d is not a mlra_dtype", a->dtype);
+  if (a->out_dtype != MLRA_BF16 && a->out_dtype != MLRA_F32)
+    return fail(MLRA_ERR_INVALID_ARG, "out_dtype %d is not a mlra_dtype", a->out_dtype);
+  if (!std::isfinite(a->sm_scale) || !std::isfinite(a->alpha))
+    return fail(MLRA_ERR_INVALID_ARG, "sm_scale and alpha must be finite");
+  if (!(a->sm_scale > 0.f)) return fail(MLRA_ERR_INVALID_ARG, "sm_scale must be > 0 (got %g)", (double)a->sm_scale);
+  if (a->max_seq_len < 1) return fail(MLRA_ERR_INVALID_ARG, "max_seq_len must be >= 1 (got %d)", a->max_seq_len);
+  if (a->num_splits < 0) return fail(MLRA_ERR_INVALID_ARG, "num_splits must be >= 0 (got %d)", a->num_splits);
+  const int64_t dc = (int64_t)a->num_branches * a->branch_dim;
+  const int64_t row_need = dc + a->rope_dim;
+  if (a->row_stride < 1) return fail(MLRA_ERR_INVALID_ARG, "row_stride must be >= 1 (got %lld)", (long long)a->row_stride);
+  if (check_pointers) {
+    if (!a->q_lat || !a->q_rope || !a->kv_lat || !a->kv_rope || !a->seq_lens || !a->w_v || !a->out)
+      return fail(MLRA_ERR_INVALID_ARG, "a required pointer (q_lat, q_rope, kv_lat, kv_rope, seq_lens, w_v, out) is NULL");
+  }
+  if (a->seq_lens_host) {
+    for (int i = 0; i < a->batch; ++i) {
+      const int L = a->seq_lens_host[i];
+      if (L < 1) return fail(MLRA_ERR_INVALID_ARG, "seq_lens[%d] = %d: an empty context has no softmax", i, L);
+      if (L > a->max_seq_len) return fail(MLRA_ERR_INVALID_ARG, "seq_lens[%d] = %d exceeds max_seq_len %d", i, L, a->max_seq_len);
+    }
+  }
+  const bool paged = a->page_table != nullptr;
+  if (paged) {
+    if (!is_pow2(a->page_size)) return fail(MLRA_ERR_INVALID_ARG, "page_size must be a power of two (got %d)", a->page_size);
+    if (a->num_pages < 1) return fail(MLRA_ERR_INVALID_ARG, "num_pages must be >= 1 (got %d)", a->num_pages);
+    if ((int64_t)a->max_pages * a->page_size < a->max_seq_len)
+      return fail(MLRA_ERR_INVALID_ARG, "max_pages %d x page_size %d cannot hold max_seq_len %d", a->max_pages, a->page_size,
+                  a->max_seq_len);
+  } else {
+    if (a->seq_stride < (int64_t)(a->max_seq_len - 1) * a->row_stride + 1 && a->batch > 1)
+      return fail(MLRA_ERR_INVALID_ARG, "seq_stride %lld is smaller than max_seq_len rows of row_stride %lld",
+                  (long long)a->seq_stride, (long long)a->row_stride);
+  }
+  // Rows may hold latent and RoPE parts anywhere; they must not overlap when they share one row.
+  if (a->kv_lat && a->kv_rope) {
+    const int64_t eb = a->dtype == MLRA_BF16 ? 2 : 4;
+    const int64_t delta = (reinterpret_cast<const char*>(a->kv_rope) - reinterpret_cast<const char*>(a->kv_lat)) / eb;
+    if (delta >= 0 && delta < dc && a->rope_dim > 0)
+      return fail(MLRA_ERR_INVALID_ARG, "kv_rope overlaps the latent columns of kv_lat");
+    if (delta == dc && a->row_stride < row_need)
+      return fail(MLRA_ERR_INVALID_ARG, "row_stride %lld is smaller than d_c + d_R = %lld", (long long)a->row_stride,
+                  (long long)row_need);
+  }
+  if (!mlra::merge_supported(a->num_branches, a->branch_dim, a->head_dim))
+    return fail(MLRA_ERR_UNSUPPORTED, "latent width %lld is beyond the merge kernel's limit", (long long)dc);
+
+  Plan p;
+  p.paged = paged;
+  const int st = (a->dtype == MLRA_BF16) ? mlra::mfma_stage_tokens(a->num_branches, a->branch_dim, a->rope_dim, a->num_heads) : 0;
+  bool mfma = st > 0;
+  if (mfma) {
+    // the MFMA path moves 16-byte chunks and reads 8-element query groups
+    const bool al = aligned(a->q_lat, 16) && aligned(a->q_rope, 16) && aligned(a->kv_lat, 16) && aligned(a->kv_rope, 16) &&
+                    a->row_stride % 8 == 0 && (paged || a->seq_stride % 8 == 0);
+    if (!al) mfma = false;
+  }
+  if (!mfma && !mlra::generic_supported(a->num_branches, a->branch_dim, a->rope_dim))
+    return fail(MLRA_ERR_UNSUPPORTED, "no kernel for num_branches=%d branch_dim=%d rope_dim=%d dtype=%d", a->num_branches,
+                a->branch_dim, a->rope_dim, a->dtype);
+  p.mfma = mfma;
+  p.stage = mfma ? st : mlra::kGenericStage;
+
+  // split size: a multiple of the stage; automatic = about one group per CU over all tokens
+  int64_t split;
+  if (a->num_splits > 0) {
+    split = cdiv(a->max_seq_len, a->num_splits);
+  } else {
+    const int64_t groups_per_pass = mfma ? kTargetGroups : kTargetGroups * 4;
+    const int64_t heads_factor = mfma ? 1 : a->num_heads;   // the generic kernel has one group per head
+    split = cdiv(total_tokens_estimate(a) * heads_factor, groups_per_pass);
+  }
+  split = std::max<int64_t>(round_up(std::max<int64_t>(split, 1), p.stage), p.stage);
+  if (paged && mfma) {
+    // the split's page ids must fit the kernel's LDS cache
+    const int64_t max_split = (int64_t)(kPageCache - 1) * a->page_size / p.stage * p.stage;
+    if (max_split < p.stage) return fail(MLRA_ERR_UNSUPPORTED, "page_size %d too small for the MFMA path", a->page_size);
+    split = std::min(split, max_split);
+  }
+  p.split_tokens = (int)std::min<int64_t>(split, a->max_seq_len + (int64_t)p.stage);
+  p.num_splits = (int)cdiv(a->max_seq_len, p.split_tokens);
+  if (p.num_splits > kMaxSplits)
+    return fail(MLRA_ERR_UNSUPPORTED, "%d context splits exceed the limit %d", p.num_splits, kMaxSplits);
+  // the merge kernel keeps (m, l) of every split of 4 sequences, and their u, in 60 KiB of LDS
+  if (sizeof(float) * ((size_t)4 * a->num_branches * p.num_splits * 2 + (size_t)4 * dc) > 60 * 1024)
+    return fail(MLRA_ERR_UNSUPPORTED, "%d splits x %d branches exceed the merge kernel's LDS", p.num_splits, a->num_branches);
+  const size_t recs = (size_t)a->batch * p.num_splits * a->num_heads * a->num_branches;
+  p.ws_o_bytes = round_up(recs * a->branch_dim * sizeof(float), 256);
+  p.ws_ml_bytes = round_up(recs * 2 * sizeof(float), 256);
+  p.ws_bytes = p.ws_o_bytes + p.ws_ml_bytes;
+  *plan = p;
+  return MLRA_OK;
+}
+
+mlra_status hip_fail(hipError_t e, const char* what) {
+  return fail(MLRA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+mlra_status run_decode(const mlra_decode_args* a, void* stream_v) {
+  Plan plan;
+  mlra_status st = make_plan(a, true, &plan);
+  if (st != MLRA_OK) return st;
+  if (!a->workspace) return fail(MLRA_ERR_WORKSPACE, "workspace is NULL (need %zu bytes)", plan.ws_bytes);
+  if (a->workspace_bytes < plan.ws_bytes)
+    return fail(MLRA_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", a->workspace_bytes, plan.ws_bytes);
+  if (!aligned(a->workspace, 256)) return fail(MLRA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  hipStream_t stream = static_cast<hipStream_t>(stream_v);
+
+  const int64_t eb = a->dtype == MLRA_BF16 ? 2 : 4;
+  mlra::AttnParams p{};
+  p.q_lat = a->q_lat;
+  p.q_rope = a->q_rope;
+  p.kv_lat = static_cast<const char*>(a->kv_lat);
+  p.kv_rope = static_cast<const char*>(a->kv_rope);
+  p.row_stride_b = a->row_stride * eb;
+  p.seq_stride_b = a->seq_stride * eb;
+  p.seq_lens = a->seq_lens;
+  p.page_table = a->page_table;
+  p.max_seq_len = a->max_seq_len;
+  p.page_shift = plan.paged ? ilog2(a->page_size) : 0;
+  p.max_pages = a->max_pages;
+  p.num_pages = a->num_pages;
+  p.B = a->batch;
+  p.H = a->num_heads;
+  p.NB = a->num_branches;
+  p.DB = a->branch_dim;
+  p.DR = a->rope_dim;
+  p.q_scale = a->sm_scale * 1.4426950408889634f;
+  p.split_tokens = plan.split_tokens;
+  p.num_splits = plan.num_splits;
+  p.ws_o = static_cast<float*>(a->workspace);
+  p.ws_ml = reinterpret_cast<float*>(static_cast<char*>(a->workspace) + plan.ws_o_bytes);
+  p.error_flags = a->error_flags;
+
+  hipError_t e;
+  if (a->event_attn_begin) {
+    e = hipEventRecord(static_cast<hipEvent_t>(a->event_attn_begin), stream);
+    if (e != hipSuccess) return hip_fail(e, "hipEventRecord(begin)");
+  }
+  if (plan.mfma) e = mlra::launch_attn_mfma(p, plan.paged, plan.num_splits, stream);
+  else e = mlra::launch_attn_generic(p, plan.paged, a->dtype, plan.num_splits, stream);
+  if (e != hipSuccess) return hip_fail(e, "attention kernel launch");
+  if (a->event_attn_end) {
+    e = hipEventRecord(static_cast<hipEvent_t>(a->event_attn_end), stream);
+    if (e != hipSuccess) return hip_fail(e, "hipEventRecord(end)");
+  }
+
+  mlra::MergeParams m{};
+  m.ws_o = p.ws_o;
+  m.ws_ml = p.ws_ml;
+  m.seq_lens = a->seq_lens;
+  m.w_v = a->w_v;
+  m.out = a->out;
+  m.max_seq_len = a->max_seq_len;
+  m.B = a->batch;
+  m.H = a->num_heads;
+  m.NB = a->num_branches;
+  m.DB = a->branch_dim;
+  m.DH = a->head_dim;
+  m.split_tokens = plan.split_tokens;
+  m.num_splits = plan.num_splits;
+  m.alpha = a->alpha;
+  m.w_dtype = a->dtype;
+  m.out_dtype = a->out_dtype;
+  e = mlra::launch_merge(m, stream);
+  if (e != hipSuccess) return hip_fail(e, "merge kernel launch");
+  return ok();
+}
+
+}  // namespace
+
+struct mlra_page_pool {
+  int32_t num_pages;
+  std::vector<int32_t> free_list;   // LIFO stack: back() is handed out next
+  std::vector<uint8_t> allocated;
+};
+
+extern "C" {
+
+const char* mlra_last_error(void) { return g_last_error.c_str(); }
+
+const char* mlra_version(void) { return "mlra 0.1.0 (gfx950)"; }
+
+size_t mlra_decode_workspace_size(const mlra_decode_args* args) {
+  Plan plan;
+  if (make_plan(args, false, &plan) != MLRA_OK) return 0;
+  ok();
+  return plan.ws_bytes;
+}
+
+mlra_status mlra_decode_validate(const mlra_decode_args* args) {
+  Plan plan;
+  mlra_status st = make_plan(args, true, &plan);
+  if (st != MLRA_OK) return st;
+  if (!args->workspace) return fail(MLRA_ERR_WORKSPACE, "workspace is NULL (need %zu bytes)", plan.ws_bytes);
+  if (args->workspace_bytes < plan.ws_bytes)
+    return fail(MLRA_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", args->workspace_bytes, plan.ws_bytes);
+  if (!aligned(args->workspace, 256)) return fail(MLRA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  return ok();
+}
+
+mlra_status mlra_decode(const mlra_decode_args* args, void* stream) { return run_decode(args, stream); }
+
+mlra_status mla_decode(const mlra_decode_args* args, void* stream) {
+  if (!args) return fail(MLRA_ERR_INVALID_ARG, "args is NULL");
+  if (args->num_branches != 1)
+    return fail(MLRA_ERR_INVALID_ARG, "mla_decode needs num_branches == 1 (got %d)", args->num_branches);
+  return run_decode(args, stream);
+}
+
+mlra_status mlra_paged_append(void* pool, int64_t row_stride, int32_t row_elems, int32_t page_size, int32_t num_pages,
+                              const int32_t* page_table, int32_t max_pages, const int32_t* positions, const void* rows,
+                              int32_t batch, int32_t dtype, uint32_t* error_flags, void* stream) {
+  if (!pool || !page_table || !positions || !rows) return fail(MLRA_ERR_INVALID_ARG, "a required pointer is NULL");
+  if (batch < 1) return fail(MLRA_ERR_INVALID_ARG, "batch must be >= 1 (got %d)", batch);
+  if (dtype != MLRA_BF16 && dtype != MLRA_F32) return fail(MLRA_ERR_INVALID_ARG, "dtype %d is not a mlra_dtype", dtype);
+  if (!is_pow2(page_size)) return fail(MLRA_ERR_INVALID_ARG, "page_size must be a power of two (got %d)", page_size);
+  if (num_pages < 1 || max_pages < 1) return fail(MLRA_ERR_INVALID_ARG, "num_pages and max_pages must be >= 1");
+  if (row_elems < 1 || row_stride < row_elems)
+    return fail(MLRA_ERR_INVALID_ARG, "need 1 <= row_elems <= row_stride (got %d, %lld)", row_elems, (long long)row_stride);
+  const int eb = dtype == MLRA_BF16 ? 2 : 4;
+  hipError_t e = mlra::launch_paged_append(pool, row_stride, row_elems, page_size, num_pages, page_table, max_pages, positions,
+                                           rows, batch, eb, error_flags, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "paged append launch");
+  return ok();
+}
+
+mlra_status mlra_paged_gather(const void* pool, int64_t row_stride, int32_t row_elems, int32_t page_size, int32_t num_pages,
+                              const int32_t* page_table, int32_t max_pages, const int32_t* seq_lens, int32_t max_seq_len,
+                              int32_t batch, int32_t dtype, void* out, uint32_t* error_flags, void* stream) {
+  if (!pool || !page_table || !seq_lens || !out) return fail(MLRA_ERR_INVALID_ARG, "a required pointer is NULL");
+  if (batch < 1 || max_seq_len < 1) return fail(MLRA_ERR_INVALID_ARG, "batch and max_seq_len must be >= 1");
+  if (dtype != MLRA_BF16 && dtype != MLRA_F32) return fail(MLRA_ERR_INVALID_ARG, "dtype %d is not a mlra_dtype", dtype);
+  if (!is_pow2(page_size)) return fail(MLRA_ERR_INVALID_ARG, "page_size must be a power of two (got %d)", page_size);
+  if (num_pages < 1 || max_pages < 1) return fail(MLRA_ERR_INVALID_ARG, "num_pages and max_pages must be >= 1");
+  if (row_elems < 1 || row_stride < row_elems)
+    return fail(MLRA_ERR_INVALID_ARG, "need 1 <= row_elems <= row_stride (got %d, %lld)", row_elems, (long long)row_stride);
+  const int eb = dtype == MLRA_BF16 ? 2 : 4;
+  hipError_t e = mlra::launch_paged_gather(pool, row_stride, row_elems, page_size, num_pages, page_table, max_pages, seq_lens,
+                                           max_seq_len, batch, eb, out, error_flags, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "paged gather launch");
+  return ok();
+}
+
+mlra_status mlra_page_table_check(const int32_t* page_table, int32_t batch, int32_t max_pages, const int32_t* seq_lens,
+                                  int32_t page_size, int32_t num_pages) {
+  if (!page_table || !seq_lens) return fail(MLRA_ERR_INVALID_ARG, "page_table and seq_lens must be host pointers");
+  if (batch < 1 || max_pages < 1 || num_pages < 1) return fail(MLRA_ERR_INVALID_ARG, "batch, max_pages, num_pages must be >= 1");
+  if (!is_pow2(page_size)) return fail(MLRA_ERR_INVALID_ARG, "page_size must be a power of two (got %d)", page_size);
+  std::vector<int32_t> owner(num_pages, -1);
+  for (int b = 0; b < batch; ++b) {
+    const int L = seq_lens[b];
+    if (L < 0) return fail(MLRA_ERR_INVALID_ARG, "seq_lens[%d] = %d is negative", b, L);
+    const int64_t need = cdiv(L, page_size);
+    if (need > max_pages)
+      return fail(MLRA_ERR_INVALID_ARG, "sequence %d needs %lld pages, the table has %d", b, (long long)need, max_pages);
+    for (int64_t j = 0; j < need; ++j) {
+      const int32_t pg = page_table[(int64_t)b * max_pages + j];
+      if (pg < 0 || pg >= num_pages)
+        return fail(MLRA_ERR_INVALID_ARG, "page_table[%d][%lld] = %d is outside [0, %d)", b, (long long)j, pg, num_pages);
+      const int32_t key = b * max_pages + (int32_t)j;
+      if (owner[pg] != -1)
+        return fail(MLRA_ERR_INVALID_ARG, "page %d backs both [%d][%d] and [%d][%lld]", pg, owner[pg] / max_pages,
+                    owner[pg] % max_pages, b, (long long)j);
+      owner[pg] = key;
+    }
+  }
+  return ok();
+}
+
+mlra_status mlra_page_pool_create(int32_t num_pages, mlra_page_pool** out) {
+  if (!out) return fail(MLRA_ERR_INVALID_ARG, "out is NULL");
+  if (num_pages < 1) return fail(MLRA_ERR_INVALID_ARG, "num_pages must be >= 1 (got %d)", num_pages);
+  mlra_page_pool* p = new (std::nothrow) mlra_page_pool;
+  if (!p) return fail(MLRA_ERR_INVALID_ARG, "out of host memory");
+  p->num_pages = num_pages;
+  p->free_list.resize(num_pages);
+  for (int32_t i = 0; i < num_pages; ++i) p->free_list[i] = num_pages - 1 - i;   // page 0 on top
+  p->allocated.assign(num_pages, 0);
+  *out = p;
+  return ok();
+}
+
+mlra_status mlra_page_pool_alloc(mlra_page_pool* pool, int32_t n, int32_t* ids) {
+  if (!pool) return fail(MLRA_ERR_INVALID_ARG, "pool is NULL");
+  if (n < 0) return fail(MLRA_ERR_INVALID_ARG, "n must be >= 0 (got %d)", n);
+  if (n > 0 && !ids) return fail(MLRA_ERR_INVALID_ARG, "ids is NULL");
+  if ((size_t)n > pool->free_list.size())
+    return fail(MLRA_ERR_NO_PAGES, "asked for %d pages, %zu free", n, pool->free_list.size());
+  for (int32_t i = 0; i < n; ++i) {
+    ids[i] = pool->free_list.back();
+    pool->free_list.pop_back();
+    pool->allocated[ids[i]] = 1;
+  }
+  return ok();
+}
+
+mlra_status mlra_page_pool_free(mlra_page_pool* pool, int32_t n, const int32_t* ids) {
+  if (!pool) return fail(MLRA_ERR_INVALID_ARG, "pool is NULL");
+  if (n < 0) return fail(MLRA_ERR_INVALID_ARG, "n must be >= 0 (got %d)", n);
+  if (n > 0 && !ids) return fail(MLRA_ERR_INVALID_ARG, "ids is NULL");
+  std::vector<uint8_t> seen(pool->num_pages, 0);
+  for (int32_t i = 0; i < n; ++i) {
+    const int32_t id = ids[i];
+    if (id < 0 || id >= pool->num_pages) return fail(MLRA_ERR_INVALID_ARG, "page id %d is outside [0, %d)", id, pool->num_pages);
+    if (!pool->allocated[id]) return fail(MLRA_ERR_INVALID_ARG, "page %d is not allocated (double free?)", id);
+    if (seen[id]) return fail(MLRA_ERR_INVALID_ARG, "page %d appears twice in one free call", id);
+    seen[id] = 1;
+  }
+  for (int32_t i = 0; i < n; ++i) {
+    pool->allocated[ids[i]] = 0;
+    pool->free_list.push_back(ids[i]);
+  }
+  return ok();
+}
+
+int32_t mlra_page_pool_num_free(const mlra_page_pool* pool) { return pool ? (int32_t)pool->free_list.size() : 0; }
+
+void mlra_page_pool_destroy(mlra_page_pool* pool) { delete pool; }
+
+}  // extern "C"

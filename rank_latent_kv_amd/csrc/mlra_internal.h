@@ -1,0 +1,82 @@
+// Internal interface between the host API (mlra_api.cpp) and the HIP kernels.
+// Not part of the public ABI.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+
+#include <hip/hip_runtime_api.h>
+
+namespace mlra {
+
+// Partial softmax state written by the attention kernels, one record per
+// (sequence, split, head, branch):
+//   o  [B][S][H][NB][DB] fp32  unnormalised sum_s 2^(x_s - m) c_s
+//   ml [B][S][H][NB][2]  fp32  (m, l): reference max in log2 units and sum 2^(x_s - m)
+// where x_s = z_s * log2(e) is the logit in log2 units.
+struct AttnParams {
+  const void* q_lat;       // [B][H][NB][DB]
+  const void* q_rope;      // [B][H][DR]
+  const char* kv_lat;      // byte pointers
+  const char* kv_rope;
+  int64_t row_stride_b;    // bytes between consecutive rows
+  int64_t seq_stride_b;    // bytes between sequences (contiguous mode)
+  const int32_t* seq_lens;
+  const int32_t* page_table;
+  int32_t max_seq_len;
+  int32_t page_shift;      // log2(page_size)
+  int32_t max_pages;
+  int32_t num_pages;
+  int32_t B, H, NB, DB, DR;
+  float q_scale;           // sm_scale * log2(e)
+  int32_t split_tokens;    // tokens per split (multiple of the kernel's stage)
+  int32_t num_splits;      // splits of the longest sequence (record stride S)
+  float* ws_o;
+  float* ws_ml;
+  uint32_t* error_flags;
+};
+
+struct MergeParams {
+  const float* ws_o;
+  const float* ws_ml;
+  const int32_t* seq_lens;
+  const void* w_v;         // [H][DH][NB*DB]
+  void* out;               // [B][H][DH]
+  int32_t max_seq_len;
+  int32_t B, H, NB, DB, DH;
+  int32_t split_tokens;
+  int32_t num_splits;
+  float alpha;
+  int32_t w_dtype;         // mlra_dtype
+  int32_t out_dtype;
+};
+
+// MFMA (bf16) attention: kernel shapes compiled into the library.
+struct MfmaShape {
+  int nb, db, dr, heads;
+};
+// Stage size in tokens of the MFMA kernel for this shape (0 if not built).
+int mfma_stage_tokens(int nb, int db, int dr, int heads);
+// Launch the MFMA attention kernel; returns hipSuccess or the launch error.
+hipError_t launch_attn_mfma(const AttnParams& p, bool paged, int grid_splits, hipStream_t stream);
+
+// Generic attention kernel (fp32 or bf16 inputs, any supported dims).
+constexpr int kGenericStage = 256;
+bool generic_supported(int nb, int db, int dr);
+hipError_t launch_attn_generic(const AttnParams& p, bool paged, int dtype, int grid_splits, hipStream_t stream);
+
+// Split merge + W^V epilogue.
+bool merge_supported(int nb, int db, int dh);
+hipError_t launch_merge(const MergeParams& p, hipStream_t stream);
+
+// Paged cache copies.
+hipError_t launch_paged_append(void* pool, int64_t row_stride, int32_t row_elems, int32_t page_size,
+                               int32_t num_pages, const int32_t* page_table, int32_t max_pages,
+                               const int32_t* positions, const void* rows, int32_t batch, int32_t elem_bytes,
+                               uint32_t* error_flags, hipStream_t stream);
+hipError_t launch_paged_gather(const void* pool, int64_t row_stride, int32_t row_elems, int32_t page_size,
+                               int32_t num_pages, const int32_t* page_table, int32_t max_pages,
+                               const int32_t* seq_lens, int32_t max_seq_len, int32_t batch, int32_t elem_bytes,
+                               void* out, uint32_t* error_flags, hipStream_t stream);
+
+}  // namespace mlra

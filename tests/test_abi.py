@@ -1,0 +1,295 @@
+"""CPU tests of the C ABI: the library loads and exports every symbol the header
+declares, the ctypes struct matches the C struct, host validation returns the
+documented status for bad arguments (it runs before any HIP call, so no GPU is
+needed), and the host page allocator / page-table check behave as documented."""
+import ctypes
+import os
+import re
+import subprocess
+import tempfile
+
+import numpy as np
+import pytest
+import torch
+
+import rank_latent_kv_amd as R
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mlra.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(R.LIB_PATH), reason="libmlra.so not built")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"\b(mlra_\w+|mla_\w+)\s*\(", text)
+    return sorted(set(n for n in names if not n.startswith("mlra_status") and n != "mlra_decode_args"))
+
+
+def test_exports_every_declared_symbol():
+    names = declared_functions()
+    assert len(names) >= 14
+    lib = R.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(R.EXPORTED_SYMBOLS)
+    out = subprocess.run(["nm", "-D", "--defined-only", R.LIB_PATH], capture_output=True, text=True).stdout
+    for n in names:
+        assert re.search(rf"\bT {n}\b", out), n
+
+
+def test_version_and_clean_error():
+    assert "gfx950" in R.lib().mlra_version().decode()
+
+
+def test_struct_layout_matches_header():
+    fields = [f[0] for f in R.DecodeArgs._fields_]
+    src = ["#include <stdio.h>", "#include <stddef.h>", '#include "mlra.h"', "int main(void) {",
+           'printf("size %zu\\n", sizeof(mlra_decode_args));']
+    src += [f'printf("{f} %zu\\n", offsetof(mlra_decode_args, {f}));' for f in fields]
+    src += ["return 0; }"]
+    with tempfile.TemporaryDirectory() as d:
+        c = os.path.join(d, "layout.c")
+        exe = os.path.join(d, "layout")
+        open(c, "w").write("\n".join(src))
+        subprocess.run(["gcc", "-std=c99", "-I", os.path.join(ROOT, "include"), c, "-o", exe], check=True)
+        got = dict(line.split() for line in subprocess.run([exe], capture_output=True, text=True).stdout.splitlines())
+    assert int(got["size"]) == ctypes.sizeof(R.DecodeArgs)
+    for f in fields:
+        assert int(got[f]) == getattr(R.DecodeArgs, f).offset, f
+
+
+# ---- host validation -----------------------------------------------------------------------
+
+FAKE = 1 << 20   # 16-byte aligned stand-in device addresses; validation never dereferences them
+
+
+def base_args(B=2, H=64, NB=4, DB=32, DR=32, DH=128, L=4096, dtype=R.MLRA_BF16, lens=None):
+    a = R.DecodeArgs()
+    a.batch, a.num_heads, a.num_branches, a.branch_dim, a.rope_dim, a.head_dim = B, H, NB, DB, DR, DH
+    a.dtype = a.out_dtype = dtype
+    a.sm_scale, a.alpha = 0.125, 0.5
+    a.q_lat, a.q_rope, a.kv_lat = FAKE, FAKE * 2, FAKE * 4
+    eb = 2 if dtype == R.MLRA_BF16 else 4
+    a.kv_rope = FAKE * 4 + NB * DB * eb
+    a.row_stride = NB * DB + DR
+    a.seq_stride = L * a.row_stride
+    a.seq_lens = FAKE * 8
+    a.max_seq_len = L
+    a.w_v, a.out = FAKE * 16, FAKE * 32
+    if lens is not None:
+        base_args.keep = (ctypes.c_int32 * B)(*lens)
+        a.seq_lens_host = ctypes.cast(base_args.keep, ctypes.c_void_p).value
+    return a
+
+
+def with_workspace(a):
+    n = R.workspace_size(a)
+    a.workspace = FAKE * 64
+    a.workspace_bytes = n
+    return a
+
+
+def test_valid_args_pass_validation():
+    a = with_workspace(base_args(lens=[4096, 17]))
+    assert R.validate(a) == R.MLRA_OK
+    assert R.last_error() == ""
+
+
+def test_workspace_size_formula():
+    a = base_args(B=16, L=32768)
+    n = R.workspace_size(a)
+    # MFMA path: 128-token stages, about one work-group per CU -> 16 splits of 2048 tokens
+    recs = 16 * 16 * 64 * 4
+    expect = -(-recs * 32 * 4 // 256) * 256 + -(-recs * 2 * 4 // 256) * 256
+    assert n == expect
+    a.num_splits = 7
+    n7 = R.workspace_size(a)
+    assert n7 == -(-16 * 7 * 64 * 4 * 32 * 4 // 256) * 256 + -(-16 * 7 * 64 * 4 * 2 * 4 // 256) * 256
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("batch", 0, R.MLRA_ERR_INVALID_ARG),
+    ("num_heads", 0, R.MLRA_ERR_INVALID_ARG),
+    ("num_branches", 0, R.MLRA_ERR_INVALID_ARG),
+    ("branch_dim", 0, R.MLRA_ERR_INVALID_ARG),
+    ("head_dim", -1, R.MLRA_ERR_INVALID_ARG),
+    ("rope_dim", -2, R.MLRA_ERR_INVALID_ARG),
+    ("dtype", 7, R.MLRA_ERR_INVALID_ARG),
+    ("out_dtype", 9, R.MLRA_ERR_INVALID_ARG),
+    ("max_seq_len", 0, R.MLRA_ERR_INVALID_ARG),
+    ("num_splits", -1, R.MLRA_ERR_INVALID_ARG),
+    ("row_stride", 0, R.MLRA_ERR_INVALID_ARG),
+    ("q_lat", None, R.MLRA_ERR_INVALID_ARG),
+    ("kv_rope", None, R.MLRA_ERR_INVALID_ARG),
+    ("seq_lens", None, R.MLRA_ERR_INVALID_ARG),
+    ("w_v", None, R.MLRA_ERR_INVALID_ARG),
+    ("out", None, R.MLRA_ERR_INVALID_ARG),
+    ("sm_scale", float("nan"), R.MLRA_ERR_INVALID_ARG),
+    ("sm_scale", 0.0, R.MLRA_ERR_INVALID_ARG),
+    ("sm_scale", -0.5, R.MLRA_ERR_INVALID_ARG),
+    ("alpha", float("inf"), R.MLRA_ERR_INVALID_ARG),
+    ("seq_stride", 5, R.MLRA_ERR_INVALID_ARG),
+])
+def test_invalid_field(field, value, status):
+    a = with_workspace(base_args())
+    setattr(a, field, value)
+    assert R.validate(a) == status
+    assert R.last_error() != ""
+    # the decode entry point reports the same error without launching anything
+    assert R.lib().mlra_decode(ctypes.byref(a), None) == status
+
+
+def test_empty_context_rejected():
+    a = with_workspace_raw(base_args(lens=[4096, 0]))
+    assert R.validate(a) == R.MLRA_ERR_INVALID_ARG
+    assert "empty context" in R.last_error()
+    assert R.lib().mlra_decode_workspace_size(ctypes.byref(a)) == 0
+    a = with_workspace_raw(base_args(lens=[4097, 1]))
+    assert R.validate(a) == R.MLRA_ERR_INVALID_ARG
+
+
+def test_workspace_errors():
+    a = base_args()
+    n = R.workspace_size(a)
+    a.workspace = None
+    assert R.validate(a) == R.MLRA_ERR_WORKSPACE
+    a.workspace, a.workspace_bytes = FAKE * 64, n - 1
+    assert R.validate(a) == R.MLRA_ERR_WORKSPACE
+    a.workspace, a.workspace_bytes = FAKE * 64 + 16, n
+    assert R.validate(a) == R.MLRA_ERR_INVALID_ARG
+
+
+def test_overlapping_rope_rejected():
+    a = with_workspace(base_args())
+    a.kv_rope = a.kv_lat + 2 * 64
+    assert R.validate(a) == R.MLRA_ERR_INVALID_ARG
+    a = with_workspace(base_args())
+    a.row_stride = 100
+    a.seq_stride = 100 * 4096
+    assert R.validate(a) == R.MLRA_ERR_INVALID_ARG
+
+
+def test_mla_requires_one_branch():
+    a = with_workspace(base_args())
+    assert R.lib().mla_decode(ctypes.byref(a), None) == R.MLRA_ERR_INVALID_ARG
+    assert "num_branches" in R.last_error()
+
+
+def test_unsupported_shape():
+    a = base_args(NB=32, DB=256)
+    assert R.lib().mlra_decode_workspace_size(ctypes.byref(a)) == 0
+    assert R.validate(with_workspace_raw(a)) in (R.MLRA_ERR_UNSUPPORTED,)
+
+
+def with_workspace_raw(a):
+    a.workspace, a.workspace_bytes = FAKE * 64, 1 << 40
+    return a
+
+
+def test_generic_path_shapes_validate():
+    # shapes without an MFMA build still validate (generic kernel): 3 branches of 16, fp32
+    a = with_workspace(base_args(NB=3, DB=16, DR=8, DH=24, dtype=R.MLRA_F32))
+    assert R.validate(a) == R.MLRA_OK
+
+
+def test_paged_validation():
+    a = base_args()
+    a.page_table = FAKE * 128
+    a.page_size = 48
+    a.max_pages, a.num_pages = 100, 100
+    a.workspace, a.workspace_bytes = FAKE * 64, 1 << 40
+    assert R.validate(a) == R.MLRA_ERR_INVALID_ARG          # page size not a power of two
+    a.page_size = 64
+    a.max_pages = 10                                          # 10 x 64 < 4096
+    assert R.validate(a) == R.MLRA_ERR_INVALID_ARG
+    a.max_pages = 64
+    a.num_pages = 0
+    assert R.validate(a) == R.MLRA_ERR_INVALID_ARG
+    a.num_pages = 128
+    assert R.validate(a) == R.MLRA_OK
+
+
+def test_paged_copy_validation():
+    L = R.lib()
+    vp = FAKE
+    assert L.mlra_paged_append(None, 160, 160, 64, 4, vp, 4, vp, vp, 2, 0, None, None) == R.MLRA_ERR_INVALID_ARG
+    assert L.mlra_paged_append(vp, 160, 160, 48, 4, vp, 4, vp, vp, 2, 0, None, None) == R.MLRA_ERR_INVALID_ARG
+    assert L.mlra_paged_append(vp, 100, 160, 64, 4, vp, 4, vp, vp, 2, 0, None, None) == R.MLRA_ERR_INVALID_ARG
+    assert L.mlra_paged_append(vp, 160, 160, 64, 4, vp, 4, vp, vp, 0, 0, None, None) == R.MLRA_ERR_INVALID_ARG
+    assert L.mlra_paged_gather(vp, 160, 160, 64, 4, vp, 4, None, 64, 2, 0, vp, None, None) == R.MLRA_ERR_INVALID_ARG
+    assert L.mlra_paged_gather(vp, 160, 160, 64, 4, vp, 4, vp, 0, 2, 0, vp, None, None) == R.MLRA_ERR_INVALID_ARG
+    assert L.mlra_paged_gather(vp, 160, 160, 64, 4, vp, 4, vp, 64, 2, 3, vp, None, None) == R.MLRA_ERR_INVALID_ARG
+
+
+# ---- host page allocator and page-table check -------------------------------------------------
+
+def test_page_pool_lifo_and_exhaustion():
+    p = R.PagePool(6)
+    assert p.num_free == 6
+    assert p.alloc(3) == [0, 1, 2]
+    assert p.alloc(2) == [3, 4]
+    with pytest.raises(R.MlraError) as e:
+        p.alloc(2)
+    assert e.value.status == R.MLRA_ERR_NO_PAGES
+    assert p.num_free == 1                         # failed alloc changed nothing
+    p.free([1, 3])
+    assert p.alloc(2) == [3, 1]                    # LIFO: last freed first
+    assert p.alloc(1) == [5]
+    assert p.num_free == 0
+    p.close()
+
+
+def test_page_pool_free_errors():
+    p = R.PagePool(4)
+    ids = p.alloc(2)
+    with pytest.raises(R.MlraError):
+        p.free([2])                                # not allocated
+    with pytest.raises(R.MlraError):
+        p.free([0, 0])                             # repeated
+    with pytest.raises(R.MlraError):
+        p.free([7])                                # out of range
+    assert p.num_free == 2                         # nothing changed
+    p.free(ids)
+    with pytest.raises(R.MlraError):
+        p.free(ids)                                # double free
+    assert p.num_free == 4
+    with pytest.raises(R.MlraError):
+        R.PagePool(0)
+
+
+def test_page_pool_deterministic():
+    a, b = R.PagePool(32), R.PagePool(32)
+    rng = np.random.default_rng(0)
+    held_a, held_b = [], []
+    for _ in range(50):
+        if held_a and rng.random() < 0.4:
+            k = int(rng.integers(1, len(held_a) + 1))
+            a.free(held_a[:k]); b.free(held_b[:k])
+            held_a, held_b = held_a[k:], held_b[k:]
+        else:
+            n = int(rng.integers(0, 4))
+            if n <= a.num_free:
+                x, y = a.alloc(n), b.alloc(n)
+                assert x == y
+                held_a += x; held_b += y
+
+
+def test_page_table_check():
+    lens = torch.tensor([130, 64, 1], dtype=torch.int32)
+    pt = torch.tensor([[4, 0, 7, -1], [2, -1, -1, -1], [5, -1, -1, -1]], dtype=torch.int32)
+    R.page_table_check(pt, lens, 64, 8)
+    bad = pt.clone(); bad[0, 2] = 8
+    with pytest.raises(R.MlraError):
+        R.page_table_check(bad, lens, 64, 8)       # out of range
+    bad = pt.clone(); bad[1, 0] = 4
+    with pytest.raises(R.MlraError):
+        R.page_table_check(bad, lens, 64, 8)       # page shared by two slots
+    with pytest.raises(R.MlraError):
+        R.page_table_check(pt, torch.tensor([300, 64, 1], dtype=torch.int32), 64, 8)  # needs 5 pages > 4
+    bad = pt.clone(); bad[2, 0] = -1
+    with pytest.raises(R.MlraError):
+        R.page_table_check(bad, lens, 64, 8)
+    with pytest.raises(R.MlraError):
+        R.page_table_check(pt, lens, 48, 8)

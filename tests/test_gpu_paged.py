@@ -1,0 +1,119 @@
+"""GPU tests of the paged cache: append / gather are bit-exact against NumPy
+indexing through the page table, paged decode matches the oracle and equals the
+contiguous decode bit for bit on the same split boundaries."""
+import numpy as np
+import pytest
+import torch
+
+import rank_latent_kv_amd as R
+from rank_latent_kv_amd.workloads import PRESETS, make_inputs
+
+from gpu_helpers import DEV, f64, gpu_decode, oracle_decode, row_rel_err, say
+
+pytestmark = pytest.mark.gpu
+
+
+def small_paged(lens, seed=None, peaked=False):
+    w = PRESETS["mlra4_paged_b4_l64k_128k"].replace(batch=len(lens))
+    return w, make_inputs(w, seq_lens=lens, seed=seed, peaked=peaked)
+
+
+def test_paged_decode_matches_oracle():
+    w, inp = small_paged([3000, 9000, 64, 4097])
+    say("paged decode vs oracle")
+    y = f64(gpu_decode(w, inp))
+    err = row_rel_err(y, oracle_decode(w, inp))
+    say(f"paged err {err:.3e}")
+    assert err <= 1e-2
+
+
+def test_paged_peaked():
+    w, inp = small_paged([5000, 2048], peaked=True)
+    say("paged peaked")
+    y = f64(gpu_decode(w, inp))
+    assert row_rel_err(y, oracle_decode(w, inp)) <= 1e-2
+
+
+def test_paged_equals_contiguous_bitwise():
+    w, inp = small_paged([2500, 6000, 128])
+    pool = inp["pool"]
+    pt = inp["page_table"].numpy()
+    lens = inp["seq_lens"].numpy()
+    Lm = int(lens.max())
+    kv = torch.zeros((w.batch, Lm, pool.shape[-1]), dtype=pool.dtype)
+    flat = pool.reshape(-1, pool.shape[-1])
+    for b in range(w.batch):
+        idx = [int(pt[b][s // w.page_size]) * w.page_size + s % w.page_size for s in range(int(lens[b]))]
+        kv[b, :lens[b]] = flat[idx]
+    wc = w.replace(paged=False)
+    cinp = {"kv": kv, "q_lat": inp["q_lat"], "q_rope": inp["q_rope"], "w_v": inp["w_v"], "seq_lens": inp["seq_lens"]}
+    say("paged vs contiguous, same splits")
+    for ns in (3, 10):
+        a = gpu_decode(w, inp, num_splits=ns)
+        b = gpu_decode(wc, cinp, num_splits=ns)
+        assert torch.equal(a, b), ns
+
+
+def test_append_and_gather_bitexact():
+    rng = np.random.default_rng(3)
+    ps, P, Rw = 64, 37, 160
+    B = 4
+    pool = torch.from_numpy(rng.standard_normal((P, ps, Rw)).astype(np.float32)).to(torch.bfloat16).to(DEV)
+    perm = rng.permutation(P)
+    max_pages = 9
+    pt = np.full((B, max_pages), -1, dtype=np.int32)
+    lens = np.array([500, 64, 1, 300], dtype=np.int32)
+    off = 0
+    for b in range(B):
+        n = -(-int(lens[b]) // ps)
+        pt[b, :n] = perm[off:off + n]
+        off += n
+    R.page_table_check(torch.from_numpy(pt), torch.from_numpy(lens), ps, P)
+    pt_d = torch.from_numpy(pt).to(DEV)
+    # append the row for position lens-1 of each sequence
+    rows = torch.from_numpy(rng.standard_normal((B, Rw)).astype(np.float32)).to(torch.bfloat16).to(DEV)
+    pos = torch.from_numpy(lens - 1).to(DEV)
+    before = pool.clone()
+    say("paged append")
+    R.paged_append(pool, pt_d, pos, rows, page_size=ps)
+    torch.cuda.synchronize()
+    expect = before.clone().reshape(-1, Rw)
+    for b in range(B):
+        s = int(lens[b]) - 1
+        expect[int(pt[b][s // ps]) * ps + s % ps] = rows[b]
+    assert torch.equal(pool.reshape(-1, Rw), expect)
+    say("paged gather")
+    out = R.paged_gather(pool, pt_d, torch.from_numpy(lens).to(DEV), int(lens.max()), page_size=ps)
+    torch.cuda.synchronize()
+    flat = pool.reshape(-1, Rw).cpu()
+    for b in range(B):
+        idx = [int(pt[b][s // ps]) * ps + s % ps for s in range(int(lens[b]))]
+        assert torch.equal(out[b, :lens[b]].cpu(), flat[idx])
+        assert torch.all(out[b, lens[b]:] == 0)
+
+
+def test_append_bad_page_flagged():
+    ps, P, Rw = 64, 4, 160
+    pool = torch.zeros((P, ps, Rw), dtype=torch.bfloat16, device=DEV)
+    pt = torch.tensor([[0, 1], [2, 9]], dtype=torch.int32, device=DEV)     # 9 is outside the pool
+    rows = torch.ones((2, Rw), dtype=torch.bfloat16, device=DEV)
+    pos = torch.tensor([70, 70], dtype=torch.int32, device=DEV)
+    flags = torch.zeros(1, dtype=torch.int32, device=DEV)
+    say("append with a bad page id")
+    R.paged_append(pool, pt, pos, rows, page_size=ps, error_flags=flags)
+    torch.cuda.synchronize()
+    assert int(flags.item()) & R.FLAG_BAD_PAGE
+    assert torch.all(pool[1, 6] == 1) and int((pool != 0).sum()) == Rw
+
+
+def test_bad_page_in_decode_flagged():
+    w, inp = small_paged([300, 200])
+    inp = dict(inp)
+    pt = inp["page_table"].clone()
+    pt[1, 1] = 10 ** 6
+    inp["page_table"] = pt
+    flags = torch.zeros(1, dtype=torch.int32, device=DEV)
+    say("decode with a bad page id")
+    y = gpu_decode(w, inp, error_flags=flags)
+    assert int(flags.item()) & R.FLAG_BAD_PAGE
+    assert torch.all(torch.isfinite(y.float()))
