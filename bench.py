@@ -125,6 +125,8 @@ def main():
     ap.add_argument("--num-splits", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--calibration-copy", action="store_true",
+                    help="first run a plain 256 MiB device-to-device copy (reference for HBM byte counters)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -163,6 +165,13 @@ def main():
         a = make_step_args(w, d, caches[k % copies], outs[k % copies], ws, lens_host)
         a.num_splits = args.num_splits
         warm_args.append(a)
+    if args.calibration_copy:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     stream = torch.cuda.current_stream().cuda_stream
     L = R.lib()
     import ctypes

@@ -48,6 +48,7 @@ constexpr int kThreads = kWaves * 64;
 constexpr int kStages = 3;
 constexpr int kPageCache = 256;            // page ids of one split kept in LDS
 constexpr float kRescaleThreshold = 8.0f;  // log2 units: p = 2^x stays <= 256
+constexpr float kStageSumMax = 65536.0f;   // a lane's stage weights summing past this trigger the exact max
 
 template <int NB, int DB, int DR, int HEADS>
 struct Cfg {
@@ -78,16 +79,21 @@ struct Cfg {
   static_assert(SUB % P == 0, "phases must divide the sub-tiles");
   static_assert(DMA_PER_STAGE % kWaves == 0, "stage DMA must split evenly over waves");
   static_assert(DB % 32 == 0 && DR % 16 == 0, "MFMA tiling");
-  static_assert(NCH % 8 == 0 || NCH % 8 == 4, "chunk rotation assumes NCH = 0 or 4 mod 8");
+  static_assert((NCH % 8 == 0 && NCH >= 8) || NCH % 16 == 4, "chunk rotation assumes NCH = 0 mod 8 or 4 mod 16");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
 };
 
-// Rotation of the 16-byte chunk positions of token t inside its LDS row, so that
-// eight consecutive tokens reading the same chunk hit eight different bank groups.
+// Rotation of the 16-byte chunk positions of token t inside its LDS row. The LDS
+// serves 16 lanes of 16 bytes per cycle (64 banks of 4 bytes), so
+//  - 16 consecutive tokens reading the same chunk (score operand) and
+//  - 4 consecutive tokens (first one a multiple of 4) reading 4 consecutive
+//    chunks (transposed value operand)
+// must land in 16 different 16-byte bank groups. Row widths of 20 chunks
+// (= 4 mod 16) and 8 chunks each get a rotation with that property.
 template <int NCH>
 __device__ __forceinline__ int chunk_rot(int t) {
-  if constexpr (NCH % 8 == 0) return t & 7;
-  else return (t & 7) >> 1;
+  if constexpr (NCH % 8 == 0) return ((t >> 2) & 3) + 4 * ((t >> 1) & 1);
+  else return (t & 15) >> 2;
 }
 
 template <int NCH>
@@ -189,24 +195,67 @@ __global__ __launch_bounds__(kThreads, 1) void attn_mfma_kernel(AttnParams p) {
   const uint32_t smem_lds = (uint32_t)(uintptr_t)(lds_char*)(smem);
   const char* seq_lat = p.kv_lat + (PAGED ? 0 : (int64_t)beta * p.seq_stride_b);
   const char* seq_rope = p.kv_rope + (PAGED ? 0 : (int64_t)beta * p.seq_stride_b);
+  // Per-lane source pointers of full stages. Contiguous: the lane's row of stage 0
+  // of this split (later stages add s * ST rows). Paged: the lane's row inside its
+  // page (the page base is added per stage); pages of at most one stage hold
+  // `pslot` = the lane's page index inside the stage.
+  const int pmask = PAGED ? (1 << p.page_shift) - 1 : 0;
+  const bool big_pages = PAGED && (1 << p.page_shift) > C::ST;
+  const char* dptr[C::DMA_PER_WAVE];
+  int pslot[C::DMA_PER_WAVE];
+#pragma unroll
+  for (int i = 0; i < C::DMA_PER_WAVE; ++i) {
+    const char* sel = (drope[i] ? seq_rope : seq_lat) + dsrc[i];
+    if constexpr (PAGED) {
+      const int rin = big_pages ? dtok[i] : (dtok[i] & pmask);
+      dptr[i] = sel + (int64_t)rin * p.row_stride_b;
+      pslot[i] = big_pages ? 0 : (dtok[i] >> p.page_shift);
+    } else {
+      dptr[i] = sel + (int64_t)(t0 + dtok[i]) * p.row_stride_b;
+      pslot[i] = 0;
+    }
+  }
+  const int64_t page_bytes = PAGED ? ((int64_t)1 << p.page_shift) * p.row_stride_b : 0;
+  const int64_t stage_bytes_g = (int64_t)C::ST * p.row_stride_b;
 
   auto issue_stage = [&](int s) {
     const int tok0 = t0 + s * C::ST;
-    const bool tail = tok0 + C::ST > t1;
     const uint32_t ring = smem_lds + (uint32_t)((s % kStages) * C::STAGE_BYTES);
+    if (tok0 + C::ST <= t1) {
+      // full stage: one pointer add (and for pages one LDS page-id read) per DMA
 #pragma unroll
-    for (int i = 0; i < C::DMA_PER_WAVE; ++i) {
-      int tok = tok0 + dtok[i];
-      if (tail) tok = min(tok, t1 - 1);
-      int64_t row;
-      if constexpr (PAGED) {
-        const int pg = ptab[(tok >> p.page_shift) - first_page];
-        row = ((int64_t)pg << p.page_shift) | (tok & ((1 << p.page_shift) - 1));
-      } else {
-        row = tok;
+      for (int i = 0; i < C::DMA_PER_WAVE; ++i) {
+        const char* src;
+        if constexpr (PAGED) {
+          int pg, rin_extra;
+          if (big_pages) {
+            pg = ptab[(tok0 >> p.page_shift) - first_page];
+            rin_extra = tok0 & pmask;
+          } else {
+            pg = ptab[((tok0 - t0) >> p.page_shift) + pslot[i]];
+            rin_extra = 0;
+          }
+          src = dptr[i] + (int64_t)pg * page_bytes + (int64_t)rin_extra * p.row_stride_b;
+        } else {
+          src = dptr[i] + (int64_t)s * stage_bytes_g;
+        }
+        dma16(src, __builtin_amdgcn_readfirstlane(ring + (uint32_t)((wave + kWaves * i) * 1024)));
       }
-      const char* src = (drope[i] ? seq_rope : seq_lat) + row * p.row_stride_b + dsrc[i];
-      dma16(src, __builtin_amdgcn_readfirstlane(ring + (uint32_t)((wave + kWaves * i) * 1024)));
+    } else {
+      // ragged last stage: rows past the end repeat the last row (finite data, masked later)
+#pragma unroll
+      for (int i = 0; i < C::DMA_PER_WAVE; ++i) {
+        const int tok = min(tok0 + dtok[i], t1 - 1);
+        int64_t row;
+        if constexpr (PAGED) {
+          const int pg = ptab[(tok >> p.page_shift) - first_page];
+          row = ((int64_t)pg << p.page_shift) | (tok & pmask);
+        } else {
+          row = tok;
+        }
+        const char* src = (drope[i] ? seq_rope : seq_lat) + row * p.row_stride_b + dsrc[i];
+        dma16(src, __builtin_amdgcn_readfirstlane(ring + (uint32_t)((wave + kWaves * i) * 1024)));
+      }
     }
   };
 
@@ -227,18 +276,20 @@ __global__ __launch_bounds__(kThreads, 1) void attn_mfma_kernel(AttnParams p) {
   }
 
   // ---- per-lane LDS offsets inside a sub-tile -------------------------------------------
-  int off_r[C::KR], off_l[C::KL], off_v[C::MT];
+  int off_r[C::KR], off_l[C::KL], off_v[C::MT][2];
 #pragma unroll
   for (int k = 0; k < C::KR; ++k) off_r[k] = lds_chunk_offset<C::NCH>(n32, C::NCL + 2 * k + g);
 #pragma unroll
   for (int k = 0; k < C::KL; ++k) off_l[k] = lds_chunk_offset<C::NCH>(n32, b * (DB / 8) + 2 * k + g);
   {
     const int q4 = lane >> 4, jj = lane & 15;
-    const int tt = 4 * (q4 >> 1) + (jj >> 2);                       // token within a 8-token slab
+    const int tt = 4 * (q4 >> 1) + (jj >> 2);                       // token within an 8-token half
 #pragma unroll
     for (int mt = 0; mt < C::MT; ++mt) {
       const int f = b * DB + 32 * mt + 16 * (q4 & 1) + 4 * (jj & 3); // feature of this lane's 8-byte word
-      off_v[mt] = lds_chunk_offset<C::NCH>(tt, f >> 3) + (f & 7) * 2;
+#pragma unroll
+      for (int r = 0; r < 2; ++r)
+        off_v[mt][r] = lds_chunk_offset<C::NCH>(tt + 8 * r, f >> 3) + (f & 7) * 2;
     }
   }
 
@@ -257,6 +308,78 @@ __global__ __launch_bounds__(kThreads, 1) void attn_mfma_kernel(AttnParams p) {
   }
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
+  // ---- per-sub-tile building blocks ------------------------------------------------------
+  // scores of one 32-token sub-tile for every head group of this wave (raw units)
+  auto scores = [&](const lds_char* sub, f32x16 (&sc)[C::HPW]) {
+    bf16x8 ar[C::KR], al[C::KL];
+#pragma unroll
+    for (int k = 0; k < C::KR; ++k) ar[k] = *(const lds_bf16x8*)(sub + off_r[k]);
+#pragma unroll
+    for (int k = 0; k < C::KL; ++k) al[k] = *(const lds_bf16x8*)(sub + off_l[k]);
+#pragma unroll
+    for (int h = 0; h < C::HPW; ++h) {
+      sc[h] = f32x16{};
+#pragma unroll
+      for (int k = 0; k < C::KR; ++k) sc[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ar[k], qr[h][k], sc[h], 0, 0, 0);
+#pragma unroll
+      for (int k = 0; k < C::KL; ++k) sc[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al[k], ql[h][k], sc[h], 0, 0, 0);
+    }
+  };
+  // transposed latent block [feature x token] of one sub-tile: two 4-token halves per K-chunk
+  auto values_a = [&](const lds_char* sub, bf16x8 (&av)[2][C::MT]) {
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc) {
+#pragma unroll
+      for (int mt = 0; mt < C::MT; ++mt) {
+        const lds_char* a0 = sub + off_v[mt][0] + (16 * kc) * C::NCH * 16;
+        const lds_char* a1 = sub + off_v[mt][1] + (16 * kc) * C::NCH * 16;
+        s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(a0));
+        s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(a1));
+        bf16x4 blo = __builtin_bit_cast(bf16x4, lo), bhi = __builtin_bit_cast(bf16x4, hi);
+        av[kc][mt] = bf16x8{blo[0], blo[1], blo[2], blo[3], bhi[0], bhi[1], bhi[2], bhi[3]};
+      }
+    }
+  };
+  // lazy running max: move the reference only when a logit exceeds it by more than the threshold
+  auto maybe_rescale = [&](int h, float mx) {
+    const float xm = fmaf(mx, qs, -mref[h]);
+    if (__builtin_amdgcn_ballot_w64(xm > kRescaleThreshold) != 0) {
+      const float d = fmaxf(fmaxf(xm, other_half(xm)), 0.f);
+      const float f = __builtin_amdgcn_exp2f(-d);
+      mref[h] += d;
+      lsum[h] *= f;
+#pragma unroll
+      for (int mt = 0; mt < C::MT; ++mt) acc[h][mt] *= f;
+    }
+  };
+  // p = 2^(x - m) packed to bf16; returns ls + the sum of the packed weights
+  auto weights = [&](int h, const f32x16& x, bf16x2 (&pk)[8], float ls) -> float {
+    const float negm = -mref[h];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      f32x2 e = {__builtin_amdgcn_exp2f(fmaf(x[2 * k], qs, negm)), __builtin_amdgcn_exp2f(fmaf(x[2 * k + 1], qs, negm))};
+      pk[k] = __builtin_convertvector(e, bf16x2);
+      ls = __builtin_amdgcn_fdot2_f32_bf16(pk[k], ones, ls, false);
+    }
+    return ls;
+  };
+  // O += P.C for one sub-tile
+  auto pv = [&](int h, const bf16x2 (&pk)[8], const bf16x8 (&av)[2][C::MT]) {
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc) {
+      bf16x8 pb = {pk[4 * kc][0], pk[4 * kc][1], pk[4 * kc + 1][0], pk[4 * kc + 1][1],
+                   pk[4 * kc + 2][0], pk[4 * kc + 2][1], pk[4 * kc + 3][0], pk[4 * kc + 3][1]};
+#pragma unroll
+      for (int mt = 0; mt < C::MT; ++mt)
+        acc[h][mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[kc][mt], pb, acc[h][mt], 0, 0, 0);
+    }
+  };
+  auto accumulate = [&](int h, const f32x16& x, const bf16x8 (&av)[2][C::MT]) {
+    bf16x2 pk[8];
+    lsum[h] = weights(h, x, pk, lsum[h]);
+    pv(h, pk, av);
+  };
+
   // ---- main loop ---------------------------------------------------------------------------
   issue_stage(0);
   if (nst > 1) issue_stage(1);
@@ -268,86 +391,73 @@ __global__ __launch_bounds__(kThreads, 1) void attn_mfma_kernel(AttnParams p) {
 
     const int stage_tok0 = t0 + s * C::ST;
     const lds_char* stage = (const lds_char*)smem + (s % kStages) * C::STAGE_BYTES;
+    if (s > 0 && stage_tok0 + C::ST <= t1) {
+      // full stage after the first: every sub-tile of this wave is complete and every unit
+      // has started. Score all of them (independent MFMA chains), exponentiate against the
+      // current reference, and only if some weight came out above 2^kStageSumLog2 (seen in
+      // the lane's sum of the stage's weights) move the reference to the exact max and redo
+      // the weights; then accumulate P.C.
+      constexpr int NSW = C::SUB / C::P;
+      f32x16 sc[NSW][C::HPW];
 #pragma unroll
-    for (int u = 0; u < C::SUB; ++u) {
-      if (u % C::P != phase) continue;
-      const int valid = t1 - (stage_tok0 + 32 * u);
-      if (valid <= 0) continue;
-      const lds_char* sub = stage + u * C::SUB_BYTES;
-
-      bf16x8 ar[C::KR], al[C::KL];
-#pragma unroll
-      for (int k = 0; k < C::KR; ++k) ar[k] = *(const lds_bf16x8*)(sub + off_r[k]);
-#pragma unroll
-      for (int k = 0; k < C::KL; ++k) al[k] = *(const lds_bf16x8*)(sub + off_l[k]);
-
-      f32x16 sc[C::HPW];
+      for (int j = 0; j < NSW; ++j) scores(stage + (j * C::P + phase) * C::SUB_BYTES, sc[j]);
 #pragma unroll
       for (int h = 0; h < C::HPW; ++h) {
-        sc[h] = f32x16{};
+        bf16x2 pk[NSW][8];
+        float ls = 0.f;
 #pragma unroll
-        for (int k = 0; k < C::KR; ++k) sc[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ar[k], qr[h][k], sc[h], 0, 0, 0);
+        for (int j = 0; j < NSW; ++j) ls = weights(h, sc[j][h], pk[j], ls);
+        if (__builtin_amdgcn_ballot_w64(!(ls <= kStageSumMax)) != 0) {
+          float mx = sc[0][h][0];
 #pragma unroll
-        for (int k = 0; k < C::KL; ++k) sc[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al[k], ql[h][k], sc[h], 0, 0, 0);
-      }
-
-      // transposed latent block for P.C: [feature x token], two 4-token halves per K-chunk
-      bf16x8 av[2][C::MT];
+          for (int j = 0; j < NSW; ++j)
 #pragma unroll
-      for (int kc = 0; kc < 2; ++kc) {
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[j][h][r]);
+          maybe_rescale(h, mx);
+          ls = 0.f;
 #pragma unroll
-        for (int mt = 0; mt < C::MT; ++mt) {
-          const lds_char* a0 = sub + off_v[mt] + (16 * kc) * C::NCH * 16;
-          const lds_char* a1 = a0 + 8 * C::NCH * 16;
-          s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(a0));
-          s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(a1));
-          bf16x4 blo = __builtin_bit_cast(bf16x4, lo), bhi = __builtin_bit_cast(bf16x4, hi);
-          av[kc][mt] = bf16x8{blo[0], blo[1], blo[2], blo[3], bhi[0], bhi[1], bhi[2], bhi[3]};
+          for (int j = 0; j < NSW; ++j) ls = weights(h, sc[j][h], pk[j], ls);
+        }
+        lsum[h] += ls;
+#pragma unroll
+        for (int j = 0; j < NSW; ++j) {
+          bf16x8 av[2][C::MT];
+          values_a(stage + (j * C::P + phase) * C::SUB_BYTES, av);
+          pv(h, pk[j], av);
         }
       }
-
+    } else {
+      // first or ragged stage: one sub-tile at a time, masking tokens past the end
 #pragma unroll
-      for (int h = 0; h < C::HPW; ++h) {
-        f32x16& x = sc[h];
-        if (valid < 32) {
+      for (int u = 0; u < C::SUB; ++u) {
+        if (u % C::P != phase) continue;
+        const int valid = t1 - (stage_tok0 + 32 * u);
+        if (valid <= 0) continue;
+        const lds_char* sub = stage + u * C::SUB_BYTES;
+        f32x16 sc[C::HPW];
+        scores(sub, sc);
+        bf16x8 av[2][C::MT];
+        values_a(sub, av);
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int tok = 8 * (r >> 2) + 4 * g + (r & 3);
-            if (tok >= valid) x[r] = -INFINITY;
+        for (int h = 0; h < C::HPW; ++h) {
+          f32x16& x = sc[h];
+          if (valid < 32) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int tok = 8 * (r >> 2) + 4 * g + (r & 3);
+              if (tok >= valid) x[r] = -INFINITY;
+            }
           }
-        }
-        float mx = x[0];            // raw units (scale > 0 keeps the order)
+          float mx = x[0];            // raw units (scale > 0 keeps the order)
 #pragma unroll
-        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, x[r]);
-        if (!started[h]) {
-          mref[h] = fmaxf(mx, other_half(mx)) * qs;
-          started[h] = true;
-        } else {
-          const float xm = fmaf(mx, qs, -mref[h]);
-          if (__builtin_amdgcn_ballot_w64(xm > kRescaleThreshold) != 0) {
-            const float d = fmaxf(fmaxf(xm, other_half(xm)), 0.f);
-            const float f = __builtin_amdgcn_exp2f(-d);
-            mref[h] += d;
-            lsum[h] *= f;
-#pragma unroll
-            for (int mt = 0; mt < C::MT; ++mt) acc[h][mt] *= f;
+          for (int r = 1; r < 16; ++r) mx = fmaxf(mx, x[r]);
+          if (!started[h]) {
+            mref[h] = fmaxf(mx, other_half(mx)) * qs;
+            started[h] = true;
+          } else {
+            maybe_rescale(h, mx);
           }
-        }
-        const float negm = -mref[h];
-        bf16x2 pk[8];
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          f32x2 e = {__builtin_amdgcn_exp2f(fmaf(x[2 * k], qs, negm)), __builtin_amdgcn_exp2f(fmaf(x[2 * k + 1], qs, negm))};
-          pk[k] = __builtin_convertvector(e, bf16x2);
-          lsum[h] = __builtin_amdgcn_fdot2_f32_bf16(pk[k], ones, lsum[h], false);
-        }
-#pragma unroll
-        for (int kc = 0; kc < 2; ++kc) {
-          bf16x8 pb = {pk[4 * kc][0], pk[4 * kc][1], pk[4 * kc + 1][0], pk[4 * kc + 1][1],
-                       pk[4 * kc + 2][0], pk[4 * kc + 2][1], pk[4 * kc + 3][0], pk[4 * kc + 3][1]};
-#pragma unroll
-          for (int mt = 0; mt < C::MT; ++mt)
-            acc[h][mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[kc][mt], pb, acc[h][mt], 0, 0, 0);
+          accumulate(h, x, av);
         }
       }
     }

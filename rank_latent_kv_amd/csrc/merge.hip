@@ -9,7 +9,8 @@
 //   y[beta, i, :] = alpha * sum_b W^V_{i,b} u_{i,b} = alpha * W^V_i [u_{i,0}; ...; u_{i,nb-1}].
 //
 // One work-group per (head, block of kSeqBlock sequences): W^V_i is read once per
-// block and reused for its sequences.
+// block and reused for its sequences. The general kernel below handles fp32 W^V
+// and odd widths on the vector ALUs.
 #include <hip/hip_runtime.h>
 #include <hip/hip_bf16.h>
 
@@ -120,6 +121,172 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeParams p) {
   }
 }
 
+// MFMA variant for bf16 W^V: one work-group per (head, kSeqBlock sequences).
+//  - The W^V_i operands of this wave's output tiles, seq_lens and every split's
+//    partial state are requested up front, so the kernel pays about one memory
+//    latency. Partials of splits past a sequence's end are read (they lie inside
+//    the workspace) and discarded with selects.
+//  - Each thread merges a slice of the splits for four features of one
+//    (sequence, branch); the slices combine through LDS into u.
+//  - u is split into bf16 hi + lo parts (|u - hi - lo| <= 2^-16 |u|) and
+//      Y[seq x d_h] = U[seq x d_c] . W^V_i^T[d_c x d_h]
+//    runs on 16x16x32 MFMAs (rows past the block's sequences are zero).
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+
+constexpr int kChunk = 8;   // splits whose loads are issued together per thread
+
+template <int DC, int DH>
+__global__ __launch_bounds__(kMergeThreads) void merge_mfma_kernel(MergeParams p) {
+  constexpr int KC = DC / 32;                      // K-chunks of the epilogue
+  constexpr int NT = DH / 16;                      // 16-wide output tiles
+  constexpr int NTW = (NT + 3) / 4;                // tiles per wave
+  constexpr int ITEMS = kSeqBlock * (DC / 4);      // (sequence, 4 features)
+  constexpr int PAR = kMergeThreads / ITEMS >= 1 ? kMergeThreads / ITEMS : 1;   // threads per item
+  constexpr int UROW = DC + 8;
+  static_assert(ITEMS * PAR <= kMergeThreads || PAR == 1, "item mapping");
+  __shared__ int nsplit[kSeqBlock];
+  __shared__ float red_m[PAR][ITEMS], red_l[PAR][ITEMS];
+  __shared__ float4 red_o[PAR][ITEMS];
+  __shared__ __attribute__((aligned(16))) __bf16 uhi[16][UROW];
+  __shared__ __attribute__((aligned(16))) __bf16 ulo[16][UROW];
+
+  const int head = blockIdx.x;
+  const int beta0 = blockIdx.y * kSeqBlock;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int NB = p.NB, DB = p.DB, S = p.num_splits;
+  const int r16 = lane & 15, kg = lane >> 4;
+
+  // W^V_i operands of this wave's tiles (prefetched; used at the end)
+  const __bf16* wv = reinterpret_cast<const __bf16*>(p.w_v) + (int64_t)head * DH * DC;
+  bf16x8 wreg[NTW][KC];
+#pragma unroll
+  for (int t = 0; t < NTW; ++t) {
+    const int nt = wave + 4 * t;
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc)
+      wreg[t][kc] = nt < NT ? __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(
+                                  wv + (int64_t)(nt * 16 + r16) * DC + 32 * kc + 8 * kg))
+                            : bf16x8{};
+  }
+  if (tid < kSeqBlock) {
+    const int beta = beta0 + tid;
+    int ns = 0;
+    if (beta < p.B) {
+      int L = p.seq_lens[beta];
+      L = L < 0 ? 0 : (L > p.max_seq_len ? p.max_seq_len : L);
+      ns = (L + p.split_tokens - 1) / p.split_tokens;
+    }
+    nsplit[tid] = ns;
+  }
+  for (int i = tid; i < 16 * UROW; i += kMergeThreads) {
+    (&uhi[0][0])[i] = (__bf16)0.f;
+    (&ulo[0][0])[i] = (__bf16)0.f;
+  }
+  __syncthreads();
+
+  // 1. partial merges over this thread's splits
+  const int item = tid % ITEMS, part = tid / ITEMS;
+  const int bl = item / (DC / 4);
+  const int k = (item % (DC / 4)) * 4;
+  const int b = k / DB;
+  const int beta = beta0 + bl;
+  if (part < PAR) {
+    const int ns = nsplit[bl];
+    float m_loc = -INFINITY, l_loc = 0.f;
+    float4 o_loc = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (beta < p.B) {
+      for (int s0 = part; s0 < S; s0 += PAR * kChunk) {
+        float mv[kChunk], lv[kChunk];
+        float4 ov[kChunk];
+#pragma unroll
+        for (int j = 0; j < kChunk; ++j) {
+          const int sp = s0 + j * PAR;
+          const int spc = sp < S ? sp : S - 1;
+          const int64_t rec = (((int64_t)beta * S + spc) * p.H + head) * NB + b;
+          mv[j] = p.ws_ml[rec * 2];
+          lv[j] = p.ws_ml[rec * 2 + 1];
+          ov[j] = *reinterpret_cast<const float4*>(p.ws_o + rec * DB + (k - b * DB));
+        }
+        float mc = m_loc;
+#pragma unroll
+        for (int j = 0; j < kChunk; ++j) {
+          const bool ok = s0 + j * PAR < ns;
+          mc = ok ? fmaxf(mc, mv[j]) : mc;
+        }
+        const float fold = (m_loc == -INFINITY) ? 0.f : exp2f(m_loc - mc);
+        l_loc *= fold;
+        o_loc.x *= fold; o_loc.y *= fold; o_loc.z *= fold; o_loc.w *= fold;
+#pragma unroll
+        for (int j = 0; j < kChunk; ++j) {
+          const bool ok = s0 + j * PAR < ns;
+          const float wj = ok ? exp2f(mv[j] - mc) : 0.f;
+          l_loc += ok ? wj * lv[j] : 0.f;
+          o_loc.x += ok ? wj * ov[j].x : 0.f;
+          o_loc.y += ok ? wj * ov[j].y : 0.f;
+          o_loc.z += ok ? wj * ov[j].z : 0.f;
+          o_loc.w += ok ? wj * ov[j].w : 0.f;
+        }
+        m_loc = mc;
+      }
+    }
+    red_m[part][item] = m_loc;
+    red_l[part][item] = l_loc;
+    red_o[part][item] = o_loc;
+  }
+  __syncthreads();
+  // 2. combine the slices: u = sum_q 2^(m_q - m*) o_q / sum_q 2^(m_q - m*) l_q
+  if (tid < ITEMS) {
+    float ms = -INFINITY;
+#pragma unroll
+    for (int q = 0; q < PAR; ++q) ms = fmaxf(ms, red_m[q][tid]);
+    float den = 0.f;
+    float4 num = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int q = 0; q < PAR; ++q) {
+      const float f = (red_m[q][tid] == -INFINITY) ? 0.f : exp2f(red_m[q][tid] - ms);
+      den += f * red_l[q][tid];
+      num.x += f * red_o[q][tid].x; num.y += f * red_o[q][tid].y;
+      num.z += f * red_o[q][tid].z; num.w += f * red_o[q][tid].w;
+    }
+    const float inv = den > 0.f ? 1.f / den : 0.f;
+    const float v[4] = {num.x * inv, num.y * inv, num.z * inv, num.w * inv};
+    const int ib = tid / (DC / 4), ik = (tid % (DC / 4)) * 4;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const __bf16 hi = (__bf16)v[q];
+      uhi[ib][ik + q] = hi;
+      ulo[ib][ik + q] = (__bf16)(v[q] - (float)hi);
+    }
+  }
+  __syncthreads();
+
+  // 3. Y = U . W^T on 16x16x32 MFMAs; each wave owns every 4th 16-column tile of d_h
+#pragma unroll
+  for (int t = 0; t < NTW; ++t) {
+    const int nt = wave + 4 * t;
+    if (nt >= NT) break;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) {
+      const bf16x8 ah = *reinterpret_cast<const bf16x8*>(&uhi[r16][32 * kc + 8 * kg]);
+      const bf16x8 al = *reinterpret_cast<const bf16x8*>(&ulo[r16][32 * kc + 8 * kg]);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, wreg[t][kc], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, wreg[t][kc], acc, 0, 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int bo = 4 * kg + j;
+      const int bt = beta0 + bo;
+      if (bo >= kSeqBlock || bt >= p.B) continue;
+      const int64_t o = ((int64_t)bt * p.H + head) * DH + nt * 16 + r16;
+      const float yv = acc[j] * p.alpha;
+      if (p.out_dtype == 0) reinterpret_cast<__hip_bfloat16*>(p.out)[o] = __float2bfloat16(yv);
+      else reinterpret_cast<float*>(p.out)[o] = yv;
+    }
+  }
+}
+
 }  // namespace
 
 bool merge_supported(int nb, int db, int dh) {
@@ -128,9 +295,24 @@ bool merge_supported(int nb, int db, int dh) {
 }
 
 hipError_t launch_merge(const MergeParams& p, hipStream_t stream) {
+  dim3 grid(p.H, (p.B + kSeqBlock - 1) / kSeqBlock);
+  const int DC = p.NB * p.DB;
+  if (p.w_dtype == 0 && (reinterpret_cast<uintptr_t>(p.w_v) & 15) == 0 && p.DB % 4 == 0) {
+#define MLRA_MERGE_CASE(xDC, xDH)                                                               \
+    if (DC == xDC && p.DH == xDH) {                                                             \
+      hipLaunchKernelGGL((merge_mfma_kernel<xDC, xDH>), grid, dim3(kMergeThreads), 0, stream, p); \
+      return hipGetLastError();                                                                 \
+    }
+    MLRA_MERGE_CASE(32, 128)
+    MLRA_MERGE_CASE(64, 128)
+    MLRA_MERGE_CASE(128, 128)
+    MLRA_MERGE_CASE(256, 128)
+    MLRA_MERGE_CASE(128, 64)
+    MLRA_MERGE_CASE(128, 256)
+#undef MLRA_MERGE_CASE
+  }
   const size_t smem = sizeof(float) * ((size_t)kSeqBlock * p.NB * p.num_splits * 2 + (size_t)kSeqBlock * p.NB * p.DB);
   if (smem > 60 * 1024) return hipErrorInvalidValue;
-  dim3 grid(p.H, (p.B + kSeqBlock - 1) / kSeqBlock);
   hipLaunchKernelGGL(merge_kernel, grid, dim3(kMergeThreads), smem, stream, p);
   return hipGetLastError();
 }
