@@ -123,6 +123,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(PRESETS))
     ap.add_argument("--num-splits", type=int, default=0)
+    ap.add_argument("--batch", type=int, default=0, help="override the workload's batch (reported in config)")
+    ap.add_argument("--seq-len", type=int, default=0, help="override every sequence's length (reported in config)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--calibration-copy", action="store_true",
@@ -135,6 +137,10 @@ def main():
         sys.exit(2)
 
     w = PRESETS[args.workload]
+    if args.batch:
+        w = w.replace(batch=args.batch)
+    if args.seq_len:
+        w = w.replace(seq_len=args.seq_len, seq_len_range=None)
     dev = torch.device("cuda:0")
     inp = make_inputs(w)
     lens = inp["seq_lens"]

@@ -43,17 +43,18 @@ typedef __attribute__((address_space(3))) char lds_char;
 typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-constexpr int kWaves = 8;
-constexpr int kThreads = kWaves * 64;
-constexpr int kStages = 3;
-constexpr int kPageCache = 256;            // page ids of one split kept in LDS
+constexpr int kMaxStages = 4;
+constexpr int kLdsBytes = 160 * 1024;
+constexpr int kPageCache = 256;            // page ids of one split kept in LDS (paged mode)
 constexpr float kRescaleThreshold = 8.0f;  // log2 units: p = 2^x stays <= 256
-constexpr float kStageSumMax = 65536.0f;   // a lane's stage weights summing past this trigger the exact max
+constexpr float kStageSumMax = 65536.0f;   // a lane's sub-tile weights summing past this trigger the exact max
 
-template <int NB, int DB, int DR, int HEADS>
+template <int NB, int DB, int DR, int HEADS, int W, bool PAGED>
 struct Cfg {
+  static constexpr int WAVES = W;                        // waves per work-group
+  static constexpr int THREADS = W * 64;
   static constexpr int NHG = (HEADS + 31) / 32;          // head groups (MFMA N = 32)
-  static constexpr int WPB = kWaves / NB;                // waves per branch
+  static constexpr int WPB = W / NB;                     // waves per branch
   static constexpr int HGSPLIT = WPB < NHG ? WPB : NHG;  // head-group slots per branch
   static constexpr int HPW = NHG / HGSPLIT;              // head groups per wave
   static constexpr int P = WPB / HGSPLIT;                // token phases
@@ -65,22 +66,27 @@ struct Cfg {
   static constexpr int SUB_BYTES = 32 * NCH * 16;
   static constexpr int STAGE_BYTES = ST * NCH * 16;
   static constexpr int DMA_PER_STAGE = ST * NCH / 64;    // wave-wide 1 KiB DMA instructions
-  static constexpr int DMA_PER_WAVE = DMA_PER_STAGE / kWaves;
+  static constexpr int DMA_HI = (DMA_PER_STAGE + W - 1) / W;   // instructions of waves < DMA_SPLIT
+  static constexpr int DMA_LO = DMA_PER_STAGE / W;             // instructions of the other waves
+  static constexpr int DMA_SPLIT = DMA_PER_STAGE - DMA_LO * W;
   static constexpr int MT = DB / 32;                     // value M-tiles (32 features)
   static constexpr int KR = DR / 16;                     // RoPE K-chunks of the score
   static constexpr int KL = DB / 16;                     // latent K-chunks of the score
-  static constexpr int MERGE_WAVES = kWaves - NB * HGSPLIT;
+  static constexpr int MERGE_WAVES = W - NB * HGSPLIT;
   static constexpr int MERGE_FLOATS = HPW * (16 * MT + 2) * 64;   // per wave record
-  static constexpr int RING_BYTES = kStages * STAGE_BYTES;
+  static constexpr int PTAB_BYTES = PAGED ? kPageCache * 4 : 0;
+  static constexpr int NS_FIT = (kLdsBytes - PTAB_BYTES) / STAGE_BYTES;
+  static constexpr int NS = NS_FIT < kMaxStages ? NS_FIT : kMaxStages;   // ring depth
+  static constexpr int RING_BYTES = NS * STAGE_BYTES;
   static constexpr int MERGE_BYTES = MERGE_WAVES * MERGE_FLOATS * 4;
-  static constexpr int LDS_BYTES = (RING_BYTES > MERGE_BYTES ? RING_BYTES : MERGE_BYTES) + kPageCache * 4;
-  static_assert(kWaves % NB == 0, "branches must divide the waves");
+  static constexpr int LDS_BYTES = (RING_BYTES > MERGE_BYTES ? RING_BYTES : MERGE_BYTES) + PTAB_BYTES;
+  static_assert(W % NB == 0, "branches must divide the waves");
   static_assert(NHG % HGSPLIT == 0, "head groups must split evenly");
   static_assert(SUB % P == 0, "phases must divide the sub-tiles");
-  static_assert(DMA_PER_STAGE % kWaves == 0, "stage DMA must split evenly over waves");
   static_assert(DB % 32 == 0 && DR % 16 == 0, "MFMA tiling");
   static_assert((NCH % 8 == 0 && NCH >= 8) || NCH % 16 == 4, "chunk rotation assumes NCH = 0 mod 8 or 4 mod 16");
-  static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+  static_assert(NS >= 3, "the ring needs three stages");
+  static_assert(LDS_BYTES <= kLdsBytes, "LDS budget");
 };
 
 // Rotation of the 16-byte chunk positions of token t inside its LDS row. The LDS
@@ -122,6 +128,19 @@ __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
 }
 
+// Wait until at most `ahead` stages of `PER` DMA instructions each are outstanding.
+template <int PER, int MAXA>
+__device__ __forceinline__ void wait_dma(int ahead) {
+  if constexpr (MAXA >= 2) {
+    if (ahead >= 2) {
+      wait_vmcnt<2 * PER>();
+      return;
+    }
+  }
+  if (ahead >= 1) wait_vmcnt<PER>();
+  else wait_vmcnt<0>();
+}
+
 __device__ __forceinline__ void block_barrier() { asm volatile("s_barrier" : : : "memory"); }
 
 __device__ __forceinline__ float other_half(float x) {
@@ -133,11 +152,11 @@ __device__ __forceinline__ bf16x8 load_q8(const __bf16* src) {
   return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(src));
 }
 
-template <int NB, int DB, int DR, int HEADS, bool PAGED>
-__global__ __launch_bounds__(kThreads, 1) void attn_mfma_kernel(AttnParams p) {
-  using C = Cfg<NB, DB, DR, HEADS>;
+template <int NB, int DB, int DR, int HEADS, int W, bool PAGED>
+__global__ __launch_bounds__(W * 64, 1) void attn_mfma_kernel(AttnParams p) {
+  using C = Cfg<NB, DB, DR, HEADS, W, PAGED>;
   __shared__ __attribute__((aligned(1024))) char smem[C::LDS_BYTES];
-  int* ptab = reinterpret_cast<int*>(smem + C::LDS_BYTES - kPageCache * 4);
+  int* ptab = reinterpret_cast<int*>(smem + C::LDS_BYTES - C::PTAB_BYTES);
 
   const int beta = blockIdx.y;
   const int split = blockIdx.x;
@@ -166,7 +185,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_mfma_kernel(AttnParams p) {
   if constexpr (PAGED) {
     first_page = t0 >> p.page_shift;
     const int last_page = (t1 - 1) >> p.page_shift;
-    for (int i = tid; i <= last_page - first_page; i += kThreads) {
+    for (int i = tid; i <= last_page - first_page; i += C::THREADS) {
       int pg = p.page_table[(int64_t)beta * p.max_pages + first_page + i];
       if (pg < 0 || pg >= p.num_pages) {
         if (p.error_flags) atomicOr(p.error_flags, 2u);
@@ -178,20 +197,22 @@ __global__ __launch_bounds__(kThreads, 1) void attn_mfma_kernel(AttnParams p) {
   }
 
   // ---- DMA lane plan (stage-invariant) --------------------------------------------------
-  int dtok[C::DMA_PER_WAVE];
-  uint32_t dsrc[C::DMA_PER_WAVE];
-  bool drope[C::DMA_PER_WAVE];
-#pragma unroll
-  for (int i = 0; i < C::DMA_PER_WAVE; ++i) {
-    const int f = (wave + kWaves * i) * 64 + lane;
+  // wave w issues the stage's DMA instructions w, w + W, w + 2W, ...; the first
+  // DMA_SPLIT waves have one more than the others. Instruction i of this wave moves
+  // 16-byte LDS slot f = (w + W i) * 64 + lane: token f / NCH of the stage, chunk
+  // position f % NCH, i.e. cache chunk (position - rotation) mod NCH.
+  const int ndma = wave < C::DMA_SPLIT ? C::DMA_HI : C::DMA_LO;
+  struct DmaLane {
+    int tok;
+    int chunk;
+  };
+  auto dma_lane = [&](int i) -> DmaLane {
+    const int f = min(wave + W * i, C::DMA_PER_STAGE - 1) * 64 + lane;
     const int t = f / C::NCH;
-    const int pos = f - t * C::NCH;
-    int c = pos - chunk_rot<C::NCH>(t);
+    int c = f - t * C::NCH - chunk_rot<C::NCH>(t);
     if (c < 0) c += C::NCH;
-    dtok[i] = t;
-    drope[i] = c >= C::NCL;
-    dsrc[i] = drope[i] ? (uint32_t)(c - C::NCL) * 16u : (uint32_t)c * 16u;
-  }
+    return {t, c};
+  };
   const uint32_t smem_lds = (uint32_t)(uintptr_t)(lds_char*)(smem);
   const char* seq_lat = p.kv_lat + (PAGED ? 0 : (int64_t)beta * p.seq_stride_b);
   const char* seq_rope = p.kv_rope + (PAGED ? 0 : (int64_t)beta * p.seq_stride_b);
@@ -201,17 +222,21 @@ __global__ __launch_bounds__(kThreads, 1) void attn_mfma_kernel(AttnParams p) {
   // `pslot` = the lane's page index inside the stage.
   const int pmask = PAGED ? (1 << p.page_shift) - 1 : 0;
   const bool big_pages = PAGED && (1 << p.page_shift) > C::ST;
-  const char* dptr[C::DMA_PER_WAVE];
-  int pslot[C::DMA_PER_WAVE];
+  auto chunk_src = [&](int c) -> const char* {
+    return c >= C::NCL ? seq_rope + (c - C::NCL) * 16 : seq_lat + c * 16;
+  };
+  const char* dptr[C::DMA_HI];
+  int pslot[C::DMA_HI];
 #pragma unroll
-  for (int i = 0; i < C::DMA_PER_WAVE; ++i) {
-    const char* sel = (drope[i] ? seq_rope : seq_lat) + dsrc[i];
+  for (int i = 0; i < C::DMA_HI; ++i) {
+    const DmaLane d = dma_lane(i);
+    const char* sel = chunk_src(d.chunk);
     if constexpr (PAGED) {
-      const int rin = big_pages ? dtok[i] : (dtok[i] & pmask);
+      const int rin = big_pages ? d.tok : (d.tok & pmask);
       dptr[i] = sel + (int64_t)rin * p.row_stride_b;
-      pslot[i] = big_pages ? 0 : (dtok[i] >> p.page_shift);
+      pslot[i] = big_pages ? 0 : (d.tok >> p.page_shift);
     } else {
-      dptr[i] = sel + (int64_t)(t0 + dtok[i]) * p.row_stride_b;
+      dptr[i] = sel + (int64_t)(t0 + d.tok) * p.row_stride_b;
       pslot[i] = 0;
     }
   }
@@ -220,11 +245,12 @@ __global__ __launch_bounds__(kThreads, 1) void attn_mfma_kernel(AttnParams p) {
 
   auto issue_stage = [&](int s) {
     const int tok0 = t0 + s * C::ST;
-    const uint32_t ring = smem_lds + (uint32_t)((s % kStages) * C::STAGE_BYTES);
+    const uint32_t ring = smem_lds + (uint32_t)((s % C::NS) * C::STAGE_BYTES);
     if (tok0 + C::ST <= t1) {
       // full stage: one pointer add (and for pages one LDS page-id read) per DMA
 #pragma unroll
-      for (int i = 0; i < C::DMA_PER_WAVE; ++i) {
+      for (int i = 0; i < C::DMA_HI; ++i) {
+        if (i >= ndma) break;
         const char* src;
         if constexpr (PAGED) {
           int pg, rin_extra;
@@ -239,13 +265,15 @@ __global__ __launch_bounds__(kThreads, 1) void attn_mfma_kernel(AttnParams p) {
         } else {
           src = dptr[i] + (int64_t)s * stage_bytes_g;
         }
-        dma16(src, __builtin_amdgcn_readfirstlane(ring + (uint32_t)((wave + kWaves * i) * 1024)));
+        dma16(src, __builtin_amdgcn_readfirstlane(ring + (uint32_t)((wave + W * i) * 1024)));
       }
     } else {
       // ragged last stage: rows past the end repeat the last row (finite data, masked later)
 #pragma unroll
-      for (int i = 0; i < C::DMA_PER_WAVE; ++i) {
-        const int tok = min(tok0 + dtok[i], t1 - 1);
+      for (int i = 0; i < C::DMA_HI; ++i) {
+        if (i >= ndma) break;
+        const DmaLane d = dma_lane(i);
+        const int tok = min(tok0 + d.tok, t1 - 1);
         int64_t row;
         if constexpr (PAGED) {
           const int pg = ptab[(tok >> p.page_shift) - first_page];
@@ -253,8 +281,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_mfma_kernel(AttnParams p) {
         } else {
           row = tok;
         }
-        const char* src = (drope[i] ? seq_rope : seq_lat) + row * p.row_stride_b + dsrc[i];
-        dma16(src, __builtin_amdgcn_readfirstlane(ring + (uint32_t)((wave + kWaves * i) * 1024)));
+        const char* src = chunk_src(d.chunk) + row * p.row_stride_b;
+        dma16(src, __builtin_amdgcn_readfirstlane(ring + (uint32_t)((wave + W * i) * 1024)));
       }
     }
   };
@@ -380,87 +408,104 @@ __global__ __launch_bounds__(kThreads, 1) void attn_mfma_kernel(AttnParams p) {
     pv(h, pk, av);
   };
 
-  // ---- main loop ---------------------------------------------------------------------------
-  issue_stage(0);
-  if (nst > 1) issue_stage(1);
-  for (int s = 0; s < nst; ++s) {
-    if (s + 1 < nst) wait_vmcnt<C::DMA_PER_WAVE>();
-    else wait_vmcnt<0>();
+  // ---- stages ------------------------------------------------------------------------------
+  // wait for stage s's DMA (the younger stages already issued may stay in flight), make it
+  // visible to every wave, then refill the ring slot freed by stage s - 1 with stage
+  // s + NS - 1
+  auto begin_stage = [&](int s) {
+    const int ahead = min(nst - 1 - s, C::NS - 2);
+    if (ndma == C::DMA_HI) wait_dma<C::DMA_HI, C::NS - 2>(ahead);
+    else wait_dma<C::DMA_LO, C::NS - 2>(ahead);
     block_barrier();
-    if (s + 2 < nst) issue_stage(s + 2);
-
+    if (s + C::NS - 1 < nst) issue_stage(s + C::NS - 1);
+  };
+  auto stage_ptr = [&](int s) { return (const lds_char*)smem + (s % C::NS) * C::STAGE_BYTES; };
+  // ragged last stage (possibly also the first): one sub-tile at a time, masking tokens past the end
+  auto slow_stage = [&](int s) {
     const int stage_tok0 = t0 + s * C::ST;
-    const lds_char* stage = (const lds_char*)smem + (s % kStages) * C::STAGE_BYTES;
-    if (s > 0 && stage_tok0 + C::ST <= t1) {
-      // full stage after the first: every sub-tile of this wave is complete and every unit
-      // has started. Score all of them (independent MFMA chains), exponentiate against the
-      // current reference, and only if some weight came out above 2^kStageSumLog2 (seen in
-      // the lane's sum of the stage's weights) move the reference to the exact max and redo
-      // the weights; then accumulate P.C.
-      constexpr int NSW = C::SUB / C::P;
-      f32x16 sc[NSW][C::HPW];
+    const lds_char* stage = stage_ptr(s);
 #pragma unroll
-      for (int j = 0; j < NSW; ++j) scores(stage + (j * C::P + phase) * C::SUB_BYTES, sc[j]);
+    for (int u = 0; u < C::SUB; ++u) {
+      if (u % C::P != phase) continue;
+      const int valid = t1 - (stage_tok0 + 32 * u);
+      if (valid <= 0) continue;
+      const lds_char* sub = stage + u * C::SUB_BYTES;
+      f32x16 sc[C::HPW];
+      scores(sub, sc);
+      bf16x8 av[2][C::MT];
+      values_a(sub, av);
 #pragma unroll
       for (int h = 0; h < C::HPW; ++h) {
-        bf16x2 pk[NSW][8];
-        float ls = 0.f;
+        f32x16& x = sc[h];
+        if (valid < 32) {
 #pragma unroll
-        for (int j = 0; j < NSW; ++j) ls = weights(h, sc[j][h], pk[j], ls);
-        if (__builtin_amdgcn_ballot_w64(!(ls <= kStageSumMax)) != 0) {
-          float mx = sc[0][h][0];
+          for (int r = 0; r < 16; ++r) {
+            const int tok = 8 * (r >> 2) + 4 * g + (r & 3);
+            if (tok >= valid) x[r] = -INFINITY;
+          }
+        }
+        float mx = x[0];            // raw units (scale > 0 keeps the order)
 #pragma unroll
-          for (int j = 0; j < NSW; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[j][h][r]);
+        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, x[r]);
+        if (!started[h]) {
+          mref[h] = fmaxf(mx, other_half(mx)) * qs;
+          started[h] = true;
+        } else {
           maybe_rescale(h, mx);
-          ls = 0.f;
-#pragma unroll
-          for (int j = 0; j < NSW; ++j) ls = weights(h, sc[j][h], pk[j], ls);
         }
-        lsum[h] += ls;
-#pragma unroll
-        for (int j = 0; j < NSW; ++j) {
-          bf16x8 av[2][C::MT];
-          values_a(stage + (j * C::P + phase) * C::SUB_BYTES, av);
-          pv(h, pk[j], av);
-        }
-      }
-    } else {
-      // first or ragged stage: one sub-tile at a time, masking tokens past the end
-#pragma unroll
-      for (int u = 0; u < C::SUB; ++u) {
-        if (u % C::P != phase) continue;
-        const int valid = t1 - (stage_tok0 + 32 * u);
-        if (valid <= 0) continue;
-        const lds_char* sub = stage + u * C::SUB_BYTES;
-        f32x16 sc[C::HPW];
-        scores(sub, sc);
-        bf16x8 av[2][C::MT];
-        values_a(sub, av);
-#pragma unroll
-        for (int h = 0; h < C::HPW; ++h) {
-          f32x16& x = sc[h];
-          if (valid < 32) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int tok = 8 * (r >> 2) + 4 * g + (r & 3);
-              if (tok >= valid) x[r] = -INFINITY;
-            }
-          }
-          float mx = x[0];            // raw units (scale > 0 keeps the order)
-#pragma unroll
-          for (int r = 1; r < 16; ++r) mx = fmaxf(mx, x[r]);
-          if (!started[h]) {
-            mref[h] = fmaxf(mx, other_half(mx)) * qs;
-            started[h] = true;
-          } else {
-            maybe_rescale(h, mx);
-          }
-          accumulate(h, x, av);
-        }
+        accumulate(h, x, av);
       }
     }
+  };
+  // full stage: every sub-tile of this wave is complete. Per sub-tile: score, exponentiate
+  // against the current reference, and only if some weight came out large (seen in the
+  // lane's sum of the sub-tile's weights) move the reference to the exact max and redo
+  // the weights; then P.C. The first stage of a split seeds the reference with the exact
+  // max of its first sub-tile.
+  auto fast_stage = [&](int s, bool first) {
+    const lds_char* stage = stage_ptr(s);
+    constexpr int NSW = C::SUB / C::P;
+#pragma unroll
+    for (int j = 0; j < NSW; ++j) {
+      const lds_char* sub = stage + (j * C::P + phase) * C::SUB_BYTES;
+      f32x16 sc[C::HPW];
+      scores(sub, sc);
+      bf16x8 av[2][C::MT];
+      values_a(sub, av);
+#pragma unroll
+      for (int h = 0; h < C::HPW; ++h) {
+        if (j == 0 && first) {
+          float mx = sc[h][0];
+#pragma unroll
+          for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sc[h][r]);
+          mref[h] = fmaxf(mx, other_half(mx)) * qs;
+          started[h] = true;
+        }
+        bf16x2 pk[8];
+        float ls = weights(h, sc[h], pk, 0.f);
+        if (__builtin_amdgcn_ballot_w64(!(ls <= kStageSumMax)) != 0) {
+          float mx = sc[h][0];
+#pragma unroll
+          for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sc[h][r]);
+          maybe_rescale(h, mx);
+          ls = weights(h, sc[h], pk, 0.f);
+        }
+        lsum[h] += ls;
+        pv(h, pk, av);
+      }
+    }
+  };
+
+  // ---- main loop: full stages (the first seeds the running max), ragged last stage ----------
+  const int nfull = (t1 - t0) / C::ST;       // stages with ST valid tokens
+  for (int s = 0; s < C::NS - 1 && s < nst; ++s) issue_stage(s);
+  for (int s = 0; s < nfull; ++s) {
+    begin_stage(s);
+    fast_stage(s, s == 0);
+  }
+  if (nfull < nst) {
+    begin_stage(nst - 1);
+    slow_stage(nst - 1);
   }
 
   // ---- combine halves, merge phases, write this split's partial state -----------------------
@@ -533,37 +578,38 @@ __global__ __launch_bounds__(kThreads, 1) void attn_mfma_kernel(AttnParams p) {
   }
 }
 
-template <int NB, int DB, int DR, int HEADS>
+template <int NB, int DB, int DR, int HEADS, int W>
 hipError_t launch_shape(const AttnParams& p, bool paged, int grid_splits, hipStream_t stream) {
   dim3 grid(grid_splits, p.B);
   if (paged)
-    hipLaunchKernelGGL((attn_mfma_kernel<NB, DB, DR, HEADS, true>), grid, dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((attn_mfma_kernel<NB, DB, DR, HEADS, W, true>), grid, dim3(W * 64), 0, stream, p);
   else
-    hipLaunchKernelGGL((attn_mfma_kernel<NB, DB, DR, HEADS, false>), grid, dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((attn_mfma_kernel<NB, DB, DR, HEADS, W, false>), grid, dim3(W * 64), 0, stream, p);
   return hipGetLastError();
 }
 
 }  // namespace
 
-// Shapes built with the MFMA path: (branches, branch width, RoPE width, heads).
+// Shapes built with the MFMA path: (branches, branch width, RoPE width, heads, waves).
 #define MLRA_MFMA_SHAPES(X) \
-  X(4, 32, 32, 64)          \
-  X(1, 128, 32, 64)         \
-  X(1, 32, 32, 16)          \
-  X(1, 32, 32, 64)          \
-  X(2, 64, 32, 64)
+  X(4, 32, 32, 64, 16)      \
+  X(1, 128, 32, 64, 8)      \
+  X(1, 32, 32, 16, 8)       \
+  X(1, 32, 32, 64, 8)       \
+  X(2, 64, 32, 64, 8)
 
 int mfma_stage_tokens(int nb, int db, int dr, int heads) {
-#define X(xNB, xDB, xDR, xH) \
-  if (nb == xNB && db == xDB && dr == xDR && heads == xH) return Cfg<xNB, xDB, xDR, xH>::ST;
+#define X(xNB, xDB, xDR, xH, xW) \
+  if (nb == xNB && db == xDB && dr == xDR && heads == xH) return Cfg<xNB, xDB, xDR, xH, xW, false>::ST;
   MLRA_MFMA_SHAPES(X)
 #undef X
   return 0;
 }
 
 hipError_t launch_attn_mfma(const AttnParams& p, bool paged, int grid_splits, hipStream_t stream) {
-#define X(xNB, xDB, xDR, xH) \
-  if (p.NB == xNB && p.DB == xDB && p.DR == xDR && p.H == xH) return launch_shape<xNB, xDB, xDR, xH>(p, paged, grid_splits, stream);
+#define X(xNB, xDB, xDR, xH, xW) \
+  if (p.NB == xNB && p.DB == xDB && p.DR == xDR && p.H == xH) \
+    return launch_shape<xNB, xDB, xDR, xH, xW>(p, paged, grid_splits, stream);
   MLRA_MFMA_SHAPES(X)
 #undef X
   return hipErrorInvalidValue;
