@@ -34,6 +34,7 @@ from rank_latent_kv_amd.workloads import PRESETS, make_inputs  # noqa: E402
 METRIC = "MLRA-4 decode tokens/s + achieved HBM TB/s (% peak), h=64 L=32k bf16"
 DEFAULT_WORKLOAD = "mlra4_b16_l32k"
 ROTATE_BYTES = 512 << 20
+CALIBRATION_BYTES = 256 << 20
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "pmc_traffic.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "rank_latent_kv_amd", "csrc", f) for f in ("attn_mfma.hip", "mlra_api.cpp")]
 
@@ -80,8 +81,9 @@ def make_step_args(w, d, cache, out, ws, lens_host, events=None):
 
 
 def cpu_baseline(w, inp, budget_s: float):
-    """The CPU oracle as it stands, on whole sequences until the time budget is
-    spent (at least one). Returns (tokens/s, sequences done, seconds, threads, y)."""
+    """The CPU oracle as it stands, on whole sequences of the batch, pass after
+    pass, until the time budget is spent (at least one sequence). Returns
+    (tokens/s, sequences done, seconds, threads, y of the first pass)."""
     from oracle import mlra_oracle as O
     try:
         from threadpoolctl import threadpool_info
@@ -92,7 +94,8 @@ def cpu_baseline(w, inp, budget_s: float):
     dc = w.latent_dim
     done, ys = 0, []
     t0 = time.perf_counter()
-    for beta in range(w.batch):
+    for step in range(10 ** 6):
+        beta = step % w.batch
         q_lat = inp["q_lat"][beta:beta + 1].double().numpy()
         q_rope = inp["q_rope"][beta:beta + 1].double().numpy()
         w_v = inp["w_v"].double().numpy()
@@ -108,12 +111,82 @@ def cpu_baseline(w, inp, budget_s: float):
             kv = inp["kv"][beta:beta + 1, :lens[beta]].double().numpy()
             y = O.mlra_decode_absorbed(q_lat, q_rope, kv[:, :, :dc], kv[:, :, dc:], lens[beta:beta + 1], w_v,
                                        w.sm_scale, w.alpha)
-        ys.append(y[0])
+        if step < w.batch:
+            ys.append(y[0])
         done += 1
         if time.perf_counter() - t0 > budget_s:
             break
     dt = time.perf_counter() - t0
     return done / dt, done, dt, threads, np.stack(ys)
+
+
+def reduce_pmc(workload: str, fetch_csv: str, write_csv: str, command: str) -> str:
+    """Turn two rocprofv3 --pmc runs of this script (FETCH_SIZE, then WRITE_SIZE,
+    both with --calibration-copy) into HBM bytes per attention launch.
+
+    Both counters are in KiB per dispatch. Each is scaled by the factor that makes
+    it read CALIBRATION_BYTES for the first three large plain device copies of the
+    run (the calibration copies; a copy reads and writes that many bytes).
+    Records the result, keyed by workload and the attention kernel's source hash,
+    in profiles/pmc_traffic.json and returns a Markdown summary."""
+    import csv
+    from rank_latent_kv_amd.workloads import default_seq_lens
+
+    def load(path, counter):
+        out = []
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] == counter:
+                    out.append((int(r["Dispatch_Id"]), r["Kernel_Name"], float(r["Counter_Value"])))
+        return sorted(out)
+
+    def calibration(rows):
+        big = [v for _, k, v in rows if "copyBuffer" in k and v * 1024 > CALIBRATION_BYTES / 8][:3]
+        if len(big) < 3:
+            raise SystemExit("no calibration copies in the counter file: run bench.py with --calibration-copy")
+        return CALIBRATION_BYTES / (1024.0 * float(np.mean(big))), big
+
+    def kernel_mean(rows, name):
+        v = [x for _, k, x in rows if name in k]
+        return float(np.mean(v)) if v else float("nan"), len(v)
+
+    fetch, write = load(fetch_csv, "FETCH_SIZE"), load(write_csv, "WRITE_SIZE")
+    ff, fbig = calibration(fetch)
+    wf, wbig = calibration(write)
+    w = PRESETS[workload]
+    ab = algorithmic_bytes(w, default_seq_lens(w).tolist())
+    lines = [f"# HBM traffic per launch, {workload}", "",
+             "Made by (two passes, FETCH_SIZE then WRITE_SIZE):", "", "```", command, "```", "",
+             f"Calibration: {CALIBRATION_BYTES >> 20} MiB device copies read FETCH_SIZE "
+             f"{', '.join('%.0f' % v for v in fbig)} KiB (factor {ff:.3f}) and WRITE_SIZE "
+             f"{', '.join('%.0f' % v for v in wbig)} KiB (factor {wf:.3f}).", "",
+             "| kernel | launches | FETCH_SIZE KiB | WRITE_SIZE KiB | scaled HBM bytes | algorithmic bytes | ratio |",
+             "|---|---|---|---|---|---|---|"]
+    entry = None
+    for kname, alg in (("attn_mfma_kernel", ab["attention_kernel"]), ("attn_generic_kernel", ab["attention_kernel"]),
+                       ("merge_mfma_kernel", None), ("merge_kernel", None)):
+        fm, n = kernel_mean(fetch, kname)
+        wm, _ = kernel_mean(write, kname)
+        if n == 0:
+            continue
+        hbm = fm * 1024 * ff + wm * 1024 * wf
+        lines.append(f"| {kname} | {n} | {fm:.0f} | {wm:.0f} | {hbm:.4g} | "
+                     f"{'%.4g' % alg if alg else '-'} | {'%.3f' % (hbm / alg) if alg else '-'} |")
+        if alg and entry is None:
+            entry = {"kernel": kname, "kernel_source_hash": kernel_source_hash(), "hbm_bytes_per_launch": hbm,
+                     "fetch_kib_per_launch": fm, "write_kib_per_launch": wm, "fetch_factor": ff,
+                     "write_factor": wf, "algorithmic_bytes_per_launch": alg, "command": command}
+    try:
+        with open(PMC_SUMMARY) as f:
+            d = json.load(f)
+    except (OSError, ValueError):
+        d = {}
+    if entry is not None:
+        d[workload] = entry
+        with open(PMC_SUMMARY, "w") as f:
+            json.dump(d, f, indent=1, sort_keys=True)
+            f.write("\n")
+    return "\n".join(lines) + "\n"
 
 
 def main():
@@ -129,7 +202,18 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--calibration-copy", action="store_true",
                     help="first run a plain 256 MiB device-to-device copy (reference for HBM byte counters)")
+    ap.add_argument("--pmc-reduce", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="no GPU run: reduce two rocprofv3 counter files of --workload into profiles/")
+    ap.add_argument("--pmc-command", default="", help="with --pmc-reduce: the command that made the files")
     args = ap.parse_args()
+
+    if args.pmc_reduce:
+        text = reduce_pmc(args.workload, args.pmc_reduce[0], args.pmc_reduce[1], args.pmc_command)
+        out = os.path.join(ROOT, "profiles", f"attn_mfma_kernel_{args.workload}_hbm_traffic.md")
+        with open(out, "w") as f:
+            f.write(text)
+        print(text)
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print(json.dumps({"error": "this build runs on one GPU only: the decode kernel is measured on one "
@@ -142,6 +226,14 @@ def main():
     if args.seq_len:
         w = w.replace(seq_len=args.seq_len, seq_len_range=None)
     dev = torch.device("cuda:0")
+    if args.calibration_copy:
+        # before any other device copy, so the counter summary can find these three
+        src = torch.empty(CALIBRATION_BYTES, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     inp = make_inputs(w)
     lens = inp["seq_lens"]
     lens_host = lens.to(torch.int32).contiguous()
@@ -171,13 +263,6 @@ def main():
         a = make_step_args(w, d, caches[k % copies], outs[k % copies], ws, lens_host)
         a.num_splits = args.num_splits
         warm_args.append(a)
-    if args.calibration_copy:
-        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
     stream = torch.cuda.current_stream().cuda_stream
     L = R.lib()
     import ctypes
@@ -237,12 +322,12 @@ def main():
     # parity of this exact launch configuration against the oracle on the sampled sequences
     if not args.no_cpu_baseline:
         tps, done, dt, threads, yref = cpu_baseline(w, inp, args.cpu_budget)
-        yg = outs[(K - 1) % copies][:done].float().cpu().double().numpy()
+        yg = outs[(K - 1) % copies][:len(yref)].float().cpu().double().numpy()
         num = np.max(np.abs(yg - yref), axis=-1)
         den = np.maximum(np.max(np.abs(yref), axis=-1), 1e-30)
         result["cpu_baseline"] = {"value": tps, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-                                  "sample": f"{done} of {w.batch} sequences, whole contexts, fp64 numpy "
-                                            f"absorbed-form oracle, {dt:.1f} s"}
+                                  "sample": f"{done} whole-context sequences (passes over the {w.batch}-sequence "
+                                            f"batch), fp64 numpy absorbed-form oracle, {dt:.1f} s"}
         result["parity_max_row_rel_err"] = float(np.max(num / den))
     print(json.dumps(result), flush=True)
 

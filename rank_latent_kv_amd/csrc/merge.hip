@@ -294,10 +294,24 @@ bool merge_supported(int nb, int db, int dh) {
   return nb >= 1 && db >= 1 && nb * db <= 4096;
 }
 
+namespace {
+bool mfma_merge_shape(int dc, int dh) {
+  return (dh == 128 && (dc == 32 || dc == 64 || dc == 128 || dc == 256)) || (dc == 128 && (dh == 64 || dh == 256));
+}
+}  // namespace
+
+bool merge_uses_mfma(int nb, int db, int dh, int w_dtype, const void* w_v) {
+  return w_dtype == 0 && (reinterpret_cast<uintptr_t>(w_v) & 15) == 0 && db % 4 == 0 && mfma_merge_shape(nb * db, dh);
+}
+
+size_t merge_lds_bytes(int nb, int db, int num_splits) {
+  return sizeof(float) * ((size_t)kSeqBlock * nb * num_splits * 2 + (size_t)kSeqBlock * nb * db);
+}
+
 hipError_t launch_merge(const MergeParams& p, hipStream_t stream) {
   dim3 grid(p.H, (p.B + kSeqBlock - 1) / kSeqBlock);
   const int DC = p.NB * p.DB;
-  if (p.w_dtype == 0 && (reinterpret_cast<uintptr_t>(p.w_v) & 15) == 0 && p.DB % 4 == 0) {
+  if (merge_uses_mfma(p.NB, p.DB, p.DH, p.w_dtype, p.w_v)) {
 #define MLRA_MERGE_CASE(xDC, xDH)                                                               \
     if (DC == xDC && p.DH == xDH) {                                                             \
       hipLaunchKernelGGL((merge_mfma_kernel<xDC, xDH>), grid, dim3(kMergeThreads), 0, stream, p); \
@@ -310,9 +324,10 @@ hipError_t launch_merge(const MergeParams& p, hipStream_t stream) {
     MLRA_MERGE_CASE(128, 64)
     MLRA_MERGE_CASE(128, 256)
 #undef MLRA_MERGE_CASE
+    return hipErrorInvalidValue;   // mfma_merge_shape and the cases above disagree
   }
-  const size_t smem = sizeof(float) * ((size_t)kSeqBlock * p.NB * p.num_splits * 2 + (size_t)kSeqBlock * p.NB * p.DB);
-  if (smem > 60 * 1024) return hipErrorInvalidValue;
+  const size_t smem = merge_lds_bytes(p.NB, p.DB, p.num_splits);
+  if (smem > kMergeLdsLimit) return hipErrorInvalidValue;
   hipLaunchKernelGGL(merge_kernel, grid, dim3(kMergeThreads), smem, stream, p);
   return hipGetLastError();
 }

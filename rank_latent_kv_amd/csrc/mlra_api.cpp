@@ -160,8 +160,9 @@ mlra_status make_plan(const mlra_decode_args* a, bool check_pointers, Plan* plan
   p.num_splits = (int)cdiv(a->max_seq_len, p.split_tokens);
   if (p.num_splits > kMaxSplits)
     return fail(MLRA_ERR_UNSUPPORTED, "%d context splits exceed the limit %d", p.num_splits, kMaxSplits);
-  // the merge kernel keeps (m, l) of every split of 4 sequences, and their u, in 60 KiB of LDS
-  if (sizeof(float) * ((size_t)4 * a->num_branches * p.num_splits * 2 + (size_t)4 * dc) > 60 * 1024)
+  // the vector-ALU merge keeps (m, l) of every split of a block of sequences in LDS
+  if (!mlra::merge_uses_mfma(a->num_branches, a->branch_dim, a->head_dim, a->dtype, a->w_v) &&
+      mlra::merge_lds_bytes(a->num_branches, a->branch_dim, p.num_splits) > mlra::kMergeLdsLimit)
     return fail(MLRA_ERR_UNSUPPORTED, "%d splits x %d branches exceed the merge kernel's LDS", p.num_splits, a->num_branches);
   const size_t recs = (size_t)a->batch * p.num_splits * a->num_heads * a->num_branches;
   p.ws_o_bytes = round_up(recs * a->branch_dim * sizeof(float), 256);

@@ -67,6 +67,11 @@ hipError_t launch_attn_generic(const AttnParams& p, bool paged, int dtype, int g
 
 // Split merge + W^V epilogue.
 bool merge_supported(int nb, int db, int dh);
+// true when the MFMA merge (no per-split LDS) runs for this shape and W^V
+bool merge_uses_mfma(int nb, int db, int dh, int w_dtype, const void* w_v);
+// LDS the vector-ALU merge needs: (m, l) of every split of a block of sequences, and their u
+size_t merge_lds_bytes(int nb, int db, int num_splits);
+constexpr size_t kMergeLdsLimit = 60 * 1024;
 hipError_t launch_merge(const MergeParams& p, hipStream_t stream);
 
 // Paged cache copies.

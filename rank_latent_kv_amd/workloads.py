@@ -116,6 +116,12 @@ def draw_seq_lens(w: Workload, rng: np.random.Generator) -> np.ndarray:
     return rng.integers(lo, hi + 1, size=w.batch, dtype=np.int64).astype(np.int32)
 
 
+def default_seq_lens(w: Workload, seed: Optional[int] = None) -> np.ndarray:
+    """The context lengths make_inputs(w, seed=seed) draws, without drawing the rest."""
+    seed = BASE_SEED + w.seed_offset if seed is None else seed
+    return draw_seq_lens(w, np.random.Generator(np.random.PCG64(seed)))
+
+
 def _plant_peaks(rng, q_lat, q_rope, kv_lat, kv_rope, seq_lens, nb, db, gain):
     """Plant strongly aligned cache rows so that a few (head, token) logits dominate.
 

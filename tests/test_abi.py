@@ -293,3 +293,26 @@ def test_page_table_check():
         R.page_table_check(bad, lens, 64, 8)
     with pytest.raises(R.MlraError):
         R.page_table_check(pt, lens, 48, 8)
+
+
+def test_split_limits_follow_the_merge_kernel():
+    """The MFMA merge (bf16, 16-byte aligned W^V) has no per-split LDS, so the
+    MLRA-4 shape takes up to 4096 one-stage splits; the vector-ALU merge (fp32
+    W^V) keeps (m, l) of every split in LDS and refuses that many."""
+    L = 4096 * 128
+    a = base_args(B=1, L=L)
+    a.num_splits = 4096
+    n = R.workspace_size(a)
+    assert n == 4096 * 64 * 4 * 32 * 4 + 4096 * 64 * 4 * 2 * 4
+    a.num_splits = 4097          # rounds up to 128-token splits again: still 4096 of them
+    assert R.workspace_size(a) == n
+    f = base_args(B=1, L=L, dtype=R.MLRA_F32)
+    f.num_splits = 4096
+    with pytest.raises(R.MlraError, match="LDS"):
+        R.workspace_size(f)
+    f.num_splits = 64
+    assert R.workspace_size(f) > 0
+    huge = base_args(B=1, L=8192 * 128)
+    huge.num_splits = 8192
+    with pytest.raises(R.MlraError, match="limit"):
+        R.workspace_size(huge)
