@@ -1,29 +1,32 @@
 // Split-context flash-decode attention for MLRA / MLA on gfx950 (bf16 inputs,
 // fp32 accumulation, MFMA 32x32x16).
 //
-// One work-group (8 waves) owns one (sequence, context split). The split's
-// cache rows stream HBM -> LDS once, through a 3-stage ring filled by
-// asynchronous LDS-DMA loads, and every query head reads them from LDS: all
-// heads share one cached latent (MLRA page "原生支持张量并行的多分支低秩注意力
-// MLRA", §1.3 step 2, MQA-style attention over the latent; §3.1, each branch
-// attends over its own latent block plus the RoPE key shared by all branches).
+// One work-group of W waves (16 for MLRA-4, 8 for the single-latent shapes) owns one
+// (sequence, context split). The split's cache rows stream HBM -> LDS once, through a
+// ring of up to four stages filled by asynchronous LDS-DMA loads, and every query head
+// reads them from LDS: all heads share one cached latent (MLRA page
+// "原生支持张量并行的多分支低秩注意力MLRA", §1.3 step 2, MQA-style attention over the
+// latent; §3.1, each branch attends over its own latent block plus the RoPE key shared
+// by all branches).
 //
-// Work split inside the group. A "unit" is (branch b, group of 32 heads). Each
-// wave owns one branch and some head groups, and possibly only every P-th
-// 32-token sub-tile (a "phase"); phases are merged in LDS at the end.
+// Work split inside the group. A "unit" is (branch b, group of 32 heads). Each wave owns
+// one branch and some head groups, and possibly only every P-th 32-token sub-tile (a
+// "phase"); phases are merged in LDS at the end.
 //
 // Per 32-token sub-tile and unit:
-//   scores  S^T[tok x head] = C_ext[tok x (d_R+d_b)] . Q_ext^T, MFMA with the
-//           exact bf16 query and fp32 accumulation; the logit in log2 units is
-//           x = S * tau*log2(e) (one fma that also subtracts the reference max);
-//   softmax lazy running max: the reference m only moves when a logit exceeds it
-//           by more than kRescaleThreshold (then O and l are rescaled); p = 2^(x-m),
-//           packed to bf16; l accumulates the packed p with a bf16 dot2 so the
-//           normaliser sums exactly the weights the P.C product uses;
-//   values  O^T[feat x head] += C_b^T[feat x tok] . P^T[tok x head], MFMA, with
-//           the transposed latent read by ds_read_b64_tr_b16.
-// Each split writes its unnormalised (o, m, l); the merge kernel combines the
-// splits (log-sum-exp) and applies W^V per branch.
+//   scores  S^T[tok x head] = C_ext[tok x (d_R+d_b)] . Q_ext^T, MFMA with the exact bf16
+//           query and fp32 accumulation; the logit in log2 units is x = S * tau*log2(e)
+//           minus the reference max, one fma;
+//   softmax lazy running max: the reference m is the exact max of the split's first
+//           sub-tile and only moves (with a rescale of O and l) when a sub-tile's
+//           weights sum past 2^16; p = 2^(x-m) is packed to bf16 and l accumulates the
+//           packed values with a bf16 dot2, so the normaliser sums exactly the weights
+//           the P.C product uses;
+//   values  O^T[feat x head] += C_b^T[feat x tok] . P^T[tok x head], MFMA, with the
+//           transposed latent read by ds_read_b64_tr_b16.
+// The score MFMAs of the next sub-tile are issued before the softmax of the current one.
+// Each split writes its unnormalised (o, m, l); the merge kernel combines the splits
+// (log-sum-exp) and applies W^V per branch.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -43,7 +46,11 @@ typedef __attribute__((address_space(3))) char lds_char;
 typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-constexpr int kMaxStages = 4;
+#ifndef MLRA_SUB_PREF
+#define MLRA_SUB_PREF 4
+#endif
+
+constexpr int kMaxStages = 8;
 constexpr int kLdsBytes = 160 * 1024;
 constexpr int kPageCache = 256;            // page ids of one split kept in LDS (paged mode)
 constexpr float kRescaleThreshold = 8.0f;  // log2 units: p = 2^x stays <= 256
@@ -58,7 +65,8 @@ struct Cfg {
   static constexpr int HGSPLIT = WPB < NHG ? WPB : NHG;  // head-group slots per branch
   static constexpr int HPW = NHG / HGSPLIT;              // head groups per wave
   static constexpr int P = WPB / HGSPLIT;                // token phases
-  static constexpr int SUB = P > 4 ? P : 4;              // 32-token sub-tiles per stage
+  static constexpr int SUB = P > MLRA_SUB_PREF ? P : MLRA_SUB_PREF;   // 32-token sub-tiles per stage
+  static constexpr int NSW = SUB / P;                    // sub-tiles of one wave per stage
   static constexpr int ST = 32 * SUB;                    // tokens per stage
   static constexpr int NCL = NB * DB / 8;                // latent 16-byte chunks per row
   static constexpr int NCR = DR / 8;                     // RoPE 16-byte chunks per row
@@ -66,9 +74,10 @@ struct Cfg {
   static constexpr int SUB_BYTES = 32 * NCH * 16;
   static constexpr int STAGE_BYTES = ST * NCH * 16;
   static constexpr int DMA_PER_STAGE = ST * NCH / 64;    // wave-wide 1 KiB DMA instructions
-  static constexpr int DMA_HI = (DMA_PER_STAGE + W - 1) / W;   // instructions of waves < DMA_SPLIT
-  static constexpr int DMA_LO = DMA_PER_STAGE / W;             // instructions of the other waves
-  static constexpr int DMA_SPLIT = DMA_PER_STAGE - DMA_LO * W;
+  static constexpr int DW = W;                                         // DMA-issuing waves
+  static constexpr int DMA_HI = (DMA_PER_STAGE + DW - 1) / DW;         // instructions of waves < DMA_SPLIT
+  static constexpr int DMA_LO = DMA_PER_STAGE / DW;                    // instructions of waves DMA_SPLIT..DW-1
+  static constexpr int DMA_SPLIT = DMA_PER_STAGE - DMA_LO * DW;
   static constexpr int MT = DB / 32;                     // value M-tiles (32 features)
   static constexpr int KR = DR / 16;                     // RoPE K-chunks of the score
   static constexpr int KL = DB / 16;                     // latent K-chunks of the score
@@ -86,6 +95,7 @@ struct Cfg {
   static_assert(DB % 32 == 0 && DR % 16 == 0, "MFMA tiling");
   static_assert((NCH % 8 == 0 && NCH >= 8) || NCH % 16 == 4, "chunk rotation assumes NCH = 0 mod 8 or 4 mod 16");
   static_assert(NS >= 3, "the ring needs three stages");
+  static_assert(DMA_HI * (NS - 2) < 64, "vmcnt range of the DMA waits");
   static_assert(LDS_BYTES <= kLdsBytes, "LDS budget");
 };
 
@@ -128,17 +138,18 @@ __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
 }
 
-// Wait until at most `ahead` stages of `PER` DMA instructions each are outstanding.
+// Wait until at most `ahead` (<= MAXA) stages of `PER` DMA instructions each are outstanding.
 template <int PER, int MAXA>
 __device__ __forceinline__ void wait_dma(int ahead) {
-  if constexpr (MAXA >= 2) {
-    if (ahead >= 2) {
-      wait_vmcnt<2 * PER>();
+  if constexpr (MAXA > 0) {
+    if (ahead >= MAXA) {
+      wait_vmcnt<PER * MAXA>();
       return;
     }
+    wait_dma<PER, MAXA - 1>(ahead);
+  } else {
+    wait_vmcnt<0>();
   }
-  if (ahead >= 1) wait_vmcnt<PER>();
-  else wait_vmcnt<0>();
 }
 
 __device__ __forceinline__ void block_barrier() { asm volatile("s_barrier" : : : "memory"); }
@@ -197,17 +208,17 @@ __global__ __launch_bounds__(W * 64, 1) void attn_mfma_kernel(AttnParams p) {
   }
 
   // ---- DMA lane plan (stage-invariant) --------------------------------------------------
-  // wave w issues the stage's DMA instructions w, w + W, w + 2W, ...; the first
+  // wave w < DW issues the stage's DMA instructions w, w + DW, w + 2 DW, ...; the first
   // DMA_SPLIT waves have one more than the others. Instruction i of this wave moves
-  // 16-byte LDS slot f = (w + W i) * 64 + lane: token f / NCH of the stage, chunk
+  // 16-byte LDS slot f = (w + DW i) * 64 + lane: token f / NCH of the stage, chunk
   // position f % NCH, i.e. cache chunk (position - rotation) mod NCH.
-  const int ndma = wave < C::DMA_SPLIT ? C::DMA_HI : C::DMA_LO;
+  const int ndma = wave >= C::DW ? 0 : (wave < C::DMA_SPLIT ? C::DMA_HI : C::DMA_LO);
   struct DmaLane {
     int tok;
     int chunk;
   };
-  auto dma_lane = [&](int i) -> DmaLane {
-    const int f = min(wave + W * i, C::DMA_PER_STAGE - 1) * 64 + lane;
+  auto dma_lane = [&](int i) __attribute__((always_inline)) -> DmaLane {
+    const int f = min(wave + C::DW * i, C::DMA_PER_STAGE - 1) * 64 + lane;
     const int t = f / C::NCH;
     int c = f - t * C::NCH - chunk_rot<C::NCH>(t);
     if (c < 0) c += C::NCH;
@@ -222,7 +233,7 @@ __global__ __launch_bounds__(W * 64, 1) void attn_mfma_kernel(AttnParams p) {
   // `pslot` = the lane's page index inside the stage.
   const int pmask = PAGED ? (1 << p.page_shift) - 1 : 0;
   const bool big_pages = PAGED && (1 << p.page_shift) > C::ST;
-  auto chunk_src = [&](int c) -> const char* {
+  auto chunk_src = [&](int c) __attribute__((always_inline)) -> const char* {
     return c >= C::NCL ? seq_rope + (c - C::NCL) * 16 : seq_lat + c * 16;
   };
   const char* dptr[C::DMA_HI];
@@ -243,7 +254,7 @@ __global__ __launch_bounds__(W * 64, 1) void attn_mfma_kernel(AttnParams p) {
   const int64_t page_bytes = PAGED ? ((int64_t)1 << p.page_shift) * p.row_stride_b : 0;
   const int64_t stage_bytes_g = (int64_t)C::ST * p.row_stride_b;
 
-  auto issue_stage = [&](int s) {
+  auto issue_stage = [&](int s) __attribute__((always_inline)) {
     const int tok0 = t0 + s * C::ST;
     const uint32_t ring = smem_lds + (uint32_t)((s % C::NS) * C::STAGE_BYTES);
     if (tok0 + C::ST <= t1) {
@@ -265,7 +276,7 @@ __global__ __launch_bounds__(W * 64, 1) void attn_mfma_kernel(AttnParams p) {
         } else {
           src = dptr[i] + (int64_t)s * stage_bytes_g;
         }
-        dma16(src, __builtin_amdgcn_readfirstlane(ring + (uint32_t)((wave + W * i) * 1024)));
+        dma16(src, __builtin_amdgcn_readfirstlane(ring + (uint32_t)((wave + C::DW * i) * 1024)));
       }
     } else {
       // ragged last stage: rows past the end repeat the last row (finite data, masked later)
@@ -282,7 +293,7 @@ __global__ __launch_bounds__(W * 64, 1) void attn_mfma_kernel(AttnParams p) {
           row = tok;
         }
         const char* src = chunk_src(d.chunk) + row * p.row_stride_b;
-        dma16(src, __builtin_amdgcn_readfirstlane(ring + (uint32_t)((wave + W * i) * 1024)));
+        dma16(src, __builtin_amdgcn_readfirstlane(ring + (uint32_t)((wave + C::DW * i) * 1024)));
       }
     }
   };
@@ -338,7 +349,7 @@ __global__ __launch_bounds__(W * 64, 1) void attn_mfma_kernel(AttnParams p) {
 
   // ---- per-sub-tile building blocks ------------------------------------------------------
   // scores of one 32-token sub-tile for every head group of this wave (raw units)
-  auto scores = [&](const lds_char* sub, f32x16 (&sc)[C::HPW]) {
+  auto scores = [&](const lds_char* sub, f32x16 (&sc)[C::HPW]) __attribute__((always_inline)) {
     bf16x8 ar[C::KR], al[C::KL];
 #pragma unroll
     for (int k = 0; k < C::KR; ++k) ar[k] = *(const lds_bf16x8*)(sub + off_r[k]);
@@ -354,7 +365,7 @@ __global__ __launch_bounds__(W * 64, 1) void attn_mfma_kernel(AttnParams p) {
     }
   };
   // transposed latent block [feature x token] of one sub-tile: two 4-token halves per K-chunk
-  auto values_a = [&](const lds_char* sub, bf16x8 (&av)[2][C::MT]) {
+  auto values_a = [&](const lds_char* sub, bf16x8 (&av)[2][C::MT]) __attribute__((always_inline)) {
 #pragma unroll
     for (int kc = 0; kc < 2; ++kc) {
 #pragma unroll
@@ -369,7 +380,7 @@ __global__ __launch_bounds__(W * 64, 1) void attn_mfma_kernel(AttnParams p) {
     }
   };
   // lazy running max: move the reference only when a logit exceeds it by more than the threshold
-  auto maybe_rescale = [&](int h, float mx) {
+  auto maybe_rescale = [&](int h, float mx) __attribute__((always_inline)) {
     const float xm = fmaf(mx, qs, -mref[h]);
     if (__builtin_amdgcn_ballot_w64(xm > kRescaleThreshold) != 0) {
       const float d = fmaxf(fmaxf(xm, other_half(xm)), 0.f);
@@ -381,7 +392,7 @@ __global__ __launch_bounds__(W * 64, 1) void attn_mfma_kernel(AttnParams p) {
     }
   };
   // p = 2^(x - m) packed to bf16; returns ls + the sum of the packed weights
-  auto weights = [&](int h, const f32x16& x, bf16x2 (&pk)[8], float ls) -> float {
+  auto weights = [&](int h, const f32x16& x, bf16x2 (&pk)[8], float ls) __attribute__((always_inline)) -> float {
     const float negm = -mref[h];
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
@@ -391,8 +402,29 @@ __global__ __launch_bounds__(W * 64, 1) void attn_mfma_kernel(AttnParams p) {
     }
     return ls;
   };
+  // O += P.C for one sub-tile, reading the transposed latent one 32-feature tile at a time
+  auto pv_lds = [&](int h, const bf16x2 (&pk)[8], const lds_char* sub) __attribute__((always_inline)) {
+    bf16x8 pb[2];
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc)
+      pb[kc] = bf16x8{pk[4 * kc][0], pk[4 * kc][1], pk[4 * kc + 1][0], pk[4 * kc + 1][1],
+                      pk[4 * kc + 2][0], pk[4 * kc + 2][1], pk[4 * kc + 3][0], pk[4 * kc + 3][1]};
+#pragma unroll
+    for (int mt = 0; mt < C::MT; ++mt) {
+#pragma unroll
+      for (int kc = 0; kc < 2; ++kc) {
+        const lds_char* a0 = sub + off_v[mt][0] + (16 * kc) * C::NCH * 16;
+        const lds_char* a1 = sub + off_v[mt][1] + (16 * kc) * C::NCH * 16;
+        s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(a0));
+        s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(a1));
+        bf16x4 blo = __builtin_bit_cast(bf16x4, lo), bhi = __builtin_bit_cast(bf16x4, hi);
+        const bf16x8 a = bf16x8{blo[0], blo[1], blo[2], blo[3], bhi[0], bhi[1], bhi[2], bhi[3]};
+        acc[h][mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kc], acc[h][mt], 0, 0, 0);
+      }
+    }
+  };
   // O += P.C for one sub-tile
-  auto pv = [&](int h, const bf16x2 (&pk)[8], const bf16x8 (&av)[2][C::MT]) {
+  auto pv = [&](int h, const bf16x2 (&pk)[8], const bf16x8 (&av)[2][C::MT]) __attribute__((always_inline)) {
 #pragma unroll
     for (int kc = 0; kc < 2; ++kc) {
       bf16x8 pb = {pk[4 * kc][0], pk[4 * kc][1], pk[4 * kc + 1][0], pk[4 * kc + 1][1],
@@ -402,26 +434,16 @@ __global__ __launch_bounds__(W * 64, 1) void attn_mfma_kernel(AttnParams p) {
         acc[h][mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[kc][mt], pb, acc[h][mt], 0, 0, 0);
     }
   };
-  auto accumulate = [&](int h, const f32x16& x, const bf16x8 (&av)[2][C::MT]) {
+  auto accumulate = [&](int h, const f32x16& x, const bf16x8 (&av)[2][C::MT]) __attribute__((always_inline)) {
     bf16x2 pk[8];
     lsum[h] = weights(h, x, pk, lsum[h]);
     pv(h, pk, av);
   };
 
   // ---- stages ------------------------------------------------------------------------------
-  // wait for stage s's DMA (the younger stages already issued may stay in flight), make it
-  // visible to every wave, then refill the ring slot freed by stage s - 1 with stage
-  // s + NS - 1
-  auto begin_stage = [&](int s) {
-    const int ahead = min(nst - 1 - s, C::NS - 2);
-    if (ndma == C::DMA_HI) wait_dma<C::DMA_HI, C::NS - 2>(ahead);
-    else wait_dma<C::DMA_LO, C::NS - 2>(ahead);
-    block_barrier();
-    if (s + C::NS - 1 < nst) issue_stage(s + C::NS - 1);
-  };
-  auto stage_ptr = [&](int s) { return (const lds_char*)smem + (s % C::NS) * C::STAGE_BYTES; };
+  auto stage_ptr = [&](int s) __attribute__((always_inline)) { return (const lds_char*)smem + (s % C::NS) * C::STAGE_BYTES; };
   // ragged last stage (possibly also the first): one sub-tile at a time, masking tokens past the end
-  auto slow_stage = [&](int s) {
+  auto slow_stage = [&](int s) __attribute__((always_inline)) {
     const int stage_tok0 = t0 + s * C::ST;
     const lds_char* stage = stage_ptr(s);
 #pragma unroll
@@ -457,54 +479,67 @@ __global__ __launch_bounds__(W * 64, 1) void attn_mfma_kernel(AttnParams p) {
       }
     }
   };
-  // full stage: every sub-tile of this wave is complete. Per sub-tile: score, exponentiate
-  // against the current reference, and only if some weight came out large (seen in the
-  // lane's sum of the sub-tile's weights) move the reference to the exact max and redo
-  // the weights; then P.C. The first stage of a split seeds the reference with the exact
-  // max of its first sub-tile.
-  auto fast_stage = [&](int s, bool first) {
-    const lds_char* stage = stage_ptr(s);
-    constexpr int NSW = C::SUB / C::P;
-#pragma unroll
-    for (int j = 0; j < NSW; ++j) {
-      const lds_char* sub = stage + (j * C::P + phase) * C::SUB_BYTES;
-      f32x16 sc[C::HPW];
-      scores(sub, sc);
-      bf16x8 av[2][C::MT];
-      values_a(sub, av);
-#pragma unroll
-      for (int h = 0; h < C::HPW; ++h) {
-        if (j == 0 && first) {
-          float mx = sc[h][0];
-#pragma unroll
-          for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sc[h][r]);
-          mref[h] = fmaxf(mx, other_half(mx)) * qs;
-          started[h] = true;
-        }
-        bf16x2 pk[8];
-        float ls = weights(h, sc[h], pk, 0.f);
-        if (__builtin_amdgcn_ballot_w64(!(ls <= kStageSumMax)) != 0) {
-          float mx = sc[h][0];
-#pragma unroll
-          for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sc[h][r]);
-          maybe_rescale(h, mx);
-          ls = weights(h, sc[h], pk, 0.f);
-        }
-        lsum[h] += ls;
-        pv(h, pk, av);
-      }
-    }
-  };
 
   // ---- main loop: full stages (the first seeds the running max), ragged last stage ----------
   const int nfull = (t1 - t0) / C::ST;       // stages with ST valid tokens
-  for (int s = 0; s < C::NS - 1 && s < nst; ++s) issue_stage(s);
-  for (int s = 0; s < nfull; ++s) {
-    begin_stage(s);
-    fast_stage(s, s == 0);
+  // Software pipeline over this wave's sub-tiles k = 0, 1, ... of the full stages: the
+  // score MFMAs of sub-tile k + 1 are issued before the softmax of sub-tile k, so the
+  // matrix cores work while the vector ALUs exponentiate. A ring slot is still read by
+  // the lagging P.C of its last sub-tile after the next stage's barrier, so the refill
+  // at stage s's barrier targets the slot of stage s - 2: LOOK = NS - 2 stages ahead.
+  constexpr int LOOK = C::NS - 2;
+  for (int s = 0; s < LOOK && s < nst; ++s) issue_stage(s);
+  auto begin_piped = [&](int s) __attribute__((always_inline)) {
+    const int ahead = min(nst - 1 - s, LOOK - 1);
+    if (ndma == C::DMA_HI) wait_dma<C::DMA_HI, LOOK - 1>(ahead);
+    else wait_dma<C::DMA_LO, LOOK - 1>(ahead);
+    block_barrier();
+    if (s + LOOK < nst) issue_stage(s + LOOK);
+  };
+  auto sub_of = [&](int k) __attribute__((always_inline)) {
+    return stage_ptr(k / C::NSW) + ((k % C::NSW) * C::P + phase) * C::SUB_BYTES;
+  };
+  const int K = nfull * C::NSW;
+  // consume the scores `cur` of sub-tile k; first issue the scores of sub-tile k + 1 into `nxt`
+  auto step = [&](int k, f32x16 (&cur)[C::HPW], f32x16 (&nxt)[C::HPW]) __attribute__((always_inline)) {
+    if (k + 1 < K) {
+      if ((k + 1) % C::NSW == 0) begin_piped((k + 1) / C::NSW);
+      scores(sub_of(k + 1), nxt);
+    }
+#pragma unroll
+    for (int h = 0; h < C::HPW; ++h) {
+      bf16x2 pk[8];
+      float ls = weights(h, cur[h], pk, 0.f);
+      if (__builtin_amdgcn_ballot_w64(!(ls <= kStageSumMax)) != 0) {
+        float mx = cur[h][0];
+#pragma unroll
+        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, cur[h][r]);
+        maybe_rescale(h, mx);
+        ls = weights(h, cur[h], pk, 0.f);
+      }
+      lsum[h] += ls;
+      pv_lds(h, pk, sub_of(k));
+    }
+  };
+  if (K > 0) {
+    begin_piped(0);
+    f32x16 sa[C::HPW], sb[C::HPW];
+    scores(sub_of(0), sa);
+#pragma unroll
+    for (int h = 0; h < C::HPW; ++h) {   // the reference starts at the exact max of the first sub-tile
+      float mx = sa[h][0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sa[h][r]);
+      mref[h] = fmaxf(mx, other_half(mx)) * qs;
+      started[h] = true;
+    }
+    for (int k = 0; k < K; k += 2) {
+      step(k, sa, sb);
+      if (k + 1 < K) step(k + 1, sb, sa);
+    }
   }
   if (nfull < nst) {
-    begin_stage(nst - 1);
+    begin_piped(nst - 1);
     slow_stage(nst - 1);
   }
 
