@@ -8,9 +8,10 @@
 // summed after attention, §3.3 scaled sum; §1.3 step 3 for MLA):
 //   y[beta, i, :] = alpha * sum_b W^V_{i,b} u_{i,b} = alpha * W^V_i [u_{i,0}; ...; u_{i,nb-1}].
 //
-// One work-group per (head, block of kSeqBlock sequences): W^V_i is read once per
-// block and reused for its sequences. The general kernel below handles fp32 W^V
-// and odd widths on the vector ALUs.
+// One work-group per (head, block of sequences): W^V_i is read once per block and
+// reused for its sequences (the MFMA kernel takes 1, 2 or 4 sequences per block, fewer
+// when there are many splits to merge). The general kernel below handles fp32 W^V and
+// odd widths on the vector ALUs, with blocks of kSeqBlock sequences.
 #include <hip/hip_runtime.h>
 #include <hip/hip_bf16.h>
 
@@ -121,7 +122,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeParams p) {
   }
 }
 
-// MFMA variant for bf16 W^V: one work-group per (head, kSeqBlock sequences).
+// MFMA variant for bf16 W^V: one work-group per (head, SEQB sequences).
 //  - The W^V_i operands of this wave's output tiles, seq_lens and every split's
 //    partial state are requested up front, so the kernel pays about one memory
 //    latency. Partials of splits past a sequence's end are read (they lie inside
@@ -136,23 +137,23 @@ typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 
 constexpr int kChunk = 8;   // splits whose loads are issued together per thread
 
-template <int DC, int DH>
+template <int DC, int DH, int SEQB>
 __global__ __launch_bounds__(kMergeThreads) void merge_mfma_kernel(MergeParams p) {
   constexpr int KC = DC / 32;                      // K-chunks of the epilogue
   constexpr int NT = DH / 16;                      // 16-wide output tiles
   constexpr int NTW = (NT + 3) / 4;                // tiles per wave
-  constexpr int ITEMS = kSeqBlock * (DC / 4);      // (sequence, 4 features)
+  constexpr int ITEMS = SEQB * (DC / 4);      // (sequence, 4 features)
   constexpr int PAR = kMergeThreads / ITEMS >= 1 ? kMergeThreads / ITEMS : 1;   // threads per item
   constexpr int UROW = DC + 8;
   static_assert(ITEMS * PAR <= kMergeThreads || PAR == 1, "item mapping");
-  __shared__ int nsplit[kSeqBlock];
+  __shared__ int nsplit[SEQB];
   __shared__ float red_m[PAR][ITEMS], red_l[PAR][ITEMS];
   __shared__ float4 red_o[PAR][ITEMS];
   __shared__ __attribute__((aligned(16))) __bf16 uhi[16][UROW];
   __shared__ __attribute__((aligned(16))) __bf16 ulo[16][UROW];
 
   const int head = blockIdx.x;
-  const int beta0 = blockIdx.y * kSeqBlock;
+  const int beta0 = blockIdx.y * SEQB;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int NB = p.NB, DB = p.DB, S = p.num_splits;
   const int r16 = lane & 15, kg = lane >> 4;
@@ -169,7 +170,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_mfma_kernel(MergeParams p
                                   wv + (int64_t)(nt * 16 + r16) * DC + 32 * kc + 8 * kg))
                             : bf16x8{};
   }
-  if (tid < kSeqBlock) {
+  if (tid < SEQB) {
     const int beta = beta0 + tid;
     int ns = 0;
     if (beta < p.B) {
@@ -278,7 +279,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_mfma_kernel(MergeParams p
     for (int j = 0; j < 4; ++j) {
       const int bo = 4 * kg + j;
       const int bt = beta0 + bo;
-      if (bo >= kSeqBlock || bt >= p.B) continue;
+      if (bo >= SEQB || bt >= p.B) continue;
       const int64_t o = ((int64_t)bt * p.H + head) * DH + nt * 16 + r16;
       const float yv = acc[j] * p.alpha;
       if (p.out_dtype == 0) reinterpret_cast<__hip_bfloat16*>(p.out)[o] = __float2bfloat16(yv);
@@ -308,14 +309,31 @@ size_t merge_lds_bytes(int nb, int db, int num_splits) {
   return sizeof(float) * ((size_t)kSeqBlock * nb * num_splits * 2 + (size_t)kSeqBlock * nb * db);
 }
 
+// Sequences per work-group of the MFMA merge: W^V_i is read once per block, but a block
+// of SB sequences leaves 256 / (SB * d_c / 4) threads for each (sequence, 4 features),
+// each loading kChunk splits per round. Take the largest block whose split loads fit one
+// round; with more splits, one sequence per group (most threads per item, most groups).
+static int merge_seq_block(int dc, int num_splits) {
+  for (int sb = 4; sb > 1; sb /= 2) {
+    const int items = sb * (dc / 4);
+    const int par = kMergeThreads / items >= 1 ? kMergeThreads / items : 1;
+    if (num_splits <= par * kChunk) return sb;
+  }
+  return 1;
+}
+
 hipError_t launch_merge(const MergeParams& p, hipStream_t stream) {
   dim3 grid(p.H, (p.B + kSeqBlock - 1) / kSeqBlock);
   const int DC = p.NB * p.DB;
   if (merge_uses_mfma(p.NB, p.DB, p.DH, p.w_dtype, p.w_v)) {
-#define MLRA_MERGE_CASE(xDC, xDH)                                                               \
-    if (DC == xDC && p.DH == xDH) {                                                             \
-      hipLaunchKernelGGL((merge_mfma_kernel<xDC, xDH>), grid, dim3(kMergeThreads), 0, stream, p); \
-      return hipGetLastError();                                                                 \
+    const int sb = merge_seq_block(DC, p.num_splits);
+    const dim3 mgrid(p.H, (p.B + sb - 1) / sb);
+#define MLRA_MERGE_CASE(xDC, xDH)                                                                       \
+    if (DC == xDC && p.DH == xDH) {                                                                     \
+      if (sb == 4) hipLaunchKernelGGL((merge_mfma_kernel<xDC, xDH, 4>), mgrid, dim3(kMergeThreads), 0, stream, p); \
+      else if (sb == 2) hipLaunchKernelGGL((merge_mfma_kernel<xDC, xDH, 2>), mgrid, dim3(kMergeThreads), 0, stream, p); \
+      else hipLaunchKernelGGL((merge_mfma_kernel<xDC, xDH, 1>), mgrid, dim3(kMergeThreads), 0, stream, p); \
+      return hipGetLastError();                                                                         \
     }
     MLRA_MERGE_CASE(32, 128)
     MLRA_MERGE_CASE(64, 128)

@@ -68,6 +68,15 @@ int64_t total_tokens_estimate(const mlra_decode_args* a) {
   return (int64_t)a->batch * a->max_seq_len;
 }
 
+// Work-groups of a launch with `split`-token splits (groups past a sequence's end exit
+// at once and are not counted).
+int64_t count_groups(const mlra_decode_args* a, int64_t split) {
+  if (!a->seq_lens_host) return (int64_t)a->batch * cdiv(a->max_seq_len, split);
+  int64_t g = 0;
+  for (int i = 0; i < a->batch; ++i) g += cdiv(std::min(std::max(a->seq_lens_host[i], 1), a->max_seq_len), split);
+  return g;
+}
+
 // Validate the arguments and decide the launch. Pure host code: no HIP calls.
 mlra_status make_plan(const mlra_decode_args* a, bool check_pointers, Plan* plan) {
   if (!a) return fail(MLRA_ERR_INVALID_ARG, "args is NULL");
@@ -150,6 +159,12 @@ mlra_status make_plan(const mlra_decode_args* a, bool check_pointers, Plan* plan
     split = cdiv(total_tokens_estimate(a) * heads_factor, groups_per_pass);
   }
   split = std::max<int64_t>(round_up(std::max<int64_t>(split, 1), p.stage), p.stage);
+  if (mfma && a->num_splits == 0) {
+    // Ragged lengths round up per sequence, which can leave a few work-groups beyond
+    // one per CU; those would run as a second pass and double the kernel time. Grow
+    // the split one stage at a time until the groups fit a single pass.
+    while (split < a->max_seq_len && count_groups(a, split) > kTargetGroups) split += p.stage;
+  }
   if (paged && mfma) {
     // the split's page ids must fit the kernel's LDS cache
     const int64_t max_split = (int64_t)(kPageCache - 1) * a->page_size / p.stage * p.stage;

@@ -316,3 +316,17 @@ def test_split_limits_follow_the_merge_kernel():
     huge.num_splits = 8192
     with pytest.raises(R.MlraError, match="limit"):
         R.workspace_size(huge)
+
+
+def test_auto_split_fits_one_pass_over_the_cus():
+    """Ragged host lengths: the automatic split grows until the work-groups (the sum over
+    sequences of ceil(L / split)) fit one per CU (256 on MI355X)."""
+    lens = [84575, 128735, 91988, 118737]
+    a = base_args(B=4, L=max(lens), lens=lens)
+    n = R.workspace_size(a)
+    recs_per_split = 4 * 64 * 4
+    splits = n // (recs_per_split * 32 * 4 + recs_per_split * 2 * 4)
+    split_tokens = -(-max(lens) // splits)
+    groups = sum(-(-L // (-(-split_tokens // 128) * 128)) for L in lens)
+    assert splits == -(-max(lens) // 1792)
+    assert groups <= 256
