@@ -629,6 +629,7 @@ hipError_t launch_shape(const AttnParams& p, bool paged, int grid_splits, hipStr
 #define MLRA_MFMA_SHAPES(X) \
   X(4, 32, 32, 64, 16)      \
   X(1, 128, 32, 64, 8)      \
+  X(1, 128, 32, 16, 4)      \
   X(1, 32, 32, 16, 8)       \
   X(1, 32, 32, 64, 8)       \
   X(2, 64, 32, 64, 8)

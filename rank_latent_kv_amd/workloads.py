@@ -97,6 +97,12 @@ PRESETS: Dict[str, Workload] = {
     "mlra4_tp_shard_b64_l64k": Workload("mlra4_tp_shard_b64_l64k", batch=64, heads=16, branches=1,
                                         branch_dim=32, rope_dim=32, head_dim=128, seq_len=65536,
                                         sm_scale=1.0 / 8.0, alpha=0.5, seed_offset=4),
+    # the MLA counterpart of that rank: MLA's single latent cannot be split across tensor-
+    # parallel ranks, so a rank with 16 local heads still streams the whole 160-wide row
+    "mla_tp_shard_b64_l64k": Workload("mla_tp_shard_b64_l64k", batch=64, heads=16, branches=1,
+                                      branch_dim=128, rope_dim=32, head_dim=128, seq_len=65536,
+                                      sm_scale=1.0 / math.sqrt(160.0), alpha=1.0,
+                                      value_std=1.0 / 8.0, seed_offset=5),
 }
 
 

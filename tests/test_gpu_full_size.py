@@ -37,6 +37,7 @@ def check_sampled(w, inp, seqs, **kw):
     ("mla_b16_l32k", True, None),
     ("mlra4_paged_b4_l64k_128k", False, None),
     ("mlra4_tp_shard_b64_l64k", False, list(range(0, 64, 4)) + [63]),
+    ("mla_tp_shard_b64_l64k", True, list(range(0, 64, 8)) + [63]),
 ])
 def test_benchmark_workload_full_size(preset, mla, seqs):
     w = PRESETS[preset]

@@ -75,6 +75,13 @@ def test_tp_shard_16_heads(lens):
     check(w, make_inputs(w, seq_lens=lens))
 
 
+@pytest.mark.parametrize("lens", [[700, 2000, 64, 5]])
+def test_mla_tp_shard_16_heads(lens):
+    w = PRESETS["mla_tp_shard_b64_l64k"].replace(batch=len(lens))
+    say(f"mla tp shard h=16 lens={lens}")
+    check(w, make_inputs(w, seq_lens=lens), mla=True)
+
+
 @pytest.mark.parametrize("nb,db,heads", [(1, 32, 64), (2, 64, 64)])
 def test_other_mfma_shapes(nb, db, heads):
     w = PRESETS["mlra4_b16_l32k"].replace(batch=2, branches=nb, branch_dim=db, heads=heads, name=f"nb{nb}_db{db}")
@@ -90,7 +97,7 @@ def test_generic_bf16_shape():
 
 
 @pytest.mark.parametrize("preset,mla", [("mlra4_b16_l32k", False), ("mla_b16_l32k", True),
-                                        ("mlra4_tp_shard_b64_l64k", False)])
+                                        ("mlra4_tp_shard_b64_l64k", False), ("mla_tp_shard_b64_l64k", True)])
 def test_peaked_logits(preset, mla):
     w = PRESETS[preset].replace(batch=2)
     inp = make_inputs(w, seq_lens=[4096, 2500], peaked=True)
