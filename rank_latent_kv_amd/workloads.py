@@ -88,6 +88,11 @@ PRESETS: Dict[str, Workload] = {
                              rope_dim=32, head_dim=128, seq_len=32768,
                              sm_scale=1.0 / math.sqrt(160.0), alpha=1.0,
                              value_std=1.0 / 8.0, seed_offset=2),
+    # MLRA-2: the latent in two 64-wide branches, each head attending over both
+    "mlra2_b16_l32k": Workload("mlra2_b16_l32k", batch=16, heads=64, branches=2, branch_dim=64,
+                               rope_dim=32, head_dim=128, seq_len=32768,
+                               sm_scale=1.0 / math.sqrt(96.0), alpha=1.0 / math.sqrt(2.0),
+                               seed_offset=6),
     # long-context MLRA-4 through a scattered 64-token page table
     "mlra4_paged_b4_l64k_128k": Workload("mlra4_paged_b4_l64k_128k", batch=4, heads=64, branches=4,
                                          branch_dim=32, rope_dim=32, head_dim=128,

@@ -35,6 +35,7 @@ def check_sampled(w, inp, seqs, **kw):
 @pytest.mark.parametrize("preset,mla,seqs", [
     ("mlra4_b16_l32k", False, None),
     ("mla_b16_l32k", True, None),
+    ("mlra2_b16_l32k", False, None),
     ("mlra4_paged_b4_l64k_128k", False, None),
     ("mlra4_tp_shard_b64_l64k", False, list(range(0, 64, 4)) + [63]),
     ("mla_tp_shard_b64_l64k", True, list(range(0, 64, 8)) + [63]),

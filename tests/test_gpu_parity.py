@@ -97,7 +97,8 @@ def test_generic_bf16_shape():
 
 
 @pytest.mark.parametrize("preset,mla", [("mlra4_b16_l32k", False), ("mla_b16_l32k", True),
-                                        ("mlra4_tp_shard_b64_l64k", False), ("mla_tp_shard_b64_l64k", True)])
+                                        ("mlra4_tp_shard_b64_l64k", False), ("mla_tp_shard_b64_l64k", True),
+                                        ("mlra2_b16_l32k", False)])
 def test_peaked_logits(preset, mla):
     w = PRESETS[preset].replace(batch=2)
     inp = make_inputs(w, seq_lens=[4096, 2500], peaked=True)
