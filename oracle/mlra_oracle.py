@@ -34,6 +34,11 @@ the design notes):
     plain arguments.
   * The query attends to exactly seq_lens[b] cached rows (no causal mask is
     needed for a single decode query); an empty context is rejected.
+  * The pages name decoupled RoPE but print no rotation. Reading: the original
+    rotary position embedding, consecutive pairs (x_2j, x_2j+1) turned by
+    m * base^(-2j/d_R) at position m, base 10000; the cache stores RoPE keys
+    already rotated to their own positions and the query is rotated to the new
+    token's position.
 
 Array layouts (float64 numpy; they mirror the library's boundary):
   q_lat   [B, h, n_b, d_b]   absorbed query of each head and branch
@@ -264,6 +269,61 @@ def absorption_consistent_query(q_lat, head_dim, rng) -> Tuple[np.ndarray, np.nd
         w_k[i] = qmat[:, :dc]
     q_nope = np.einsum("inc,bic->bin", w_k, q_lat.reshape(B, h, dc))
     return q_nope, w_k
+
+
+def rope_angles(positions, rope_dim: int, base: float = 10000.0) -> np.ndarray:
+    """Rotary angles: pair j of a d_R-wide RoPE vector at position m turns by
+    m * theta_j with theta_j = base^(-2j / d_R), j = 0 .. d_R/2 - 1 (the rotary
+    position embedding behind [DS-MLA]'s decoupled RoPE; the pages do not print
+    it, so the original rotary form is taken, see the readings). fp64, shape
+    [len(positions), d_R / 2]."""
+    if rope_dim % 2:
+        raise ValueError("rope_dim must be even")
+    pos = np.asarray(positions, dtype=np.float64).reshape(-1, 1)
+    theta = base ** (-2.0 * np.arange(rope_dim // 2, dtype=np.float64) / rope_dim)
+    return pos * theta[None, :]
+
+
+def rope_rotate(x, positions, base: float = 10000.0) -> np.ndarray:
+    """Rotate consecutive pairs (x_2j, x_2j+1) of the last axis by the angle of
+    their row's position: (x_2j cos a - x_2j+1 sin a, x_2j sin a + x_2j+1 cos a).
+    x has shape [B, ..., d_R] and positions [B] (one position per leading index)."""
+    x = np.asarray(x, dtype=np.float64)
+    B, dr = x.shape[0], x.shape[-1]
+    ang = rope_angles(positions, dr, base)                       # [B, d_R/2]
+    shape = (B,) + (1,) * (x.ndim - 2) + (dr // 2,)
+    c, s = np.cos(ang).reshape(shape), np.sin(ang).reshape(shape)
+    xe, xo = x[..., 0::2], x[..., 1::2]
+    out = np.empty_like(x)
+    out[..., 0::2] = xe * c - xo * s
+    out[..., 1::2] = xe * s + xo * c
+    return out
+
+
+def absorb_query(q_nope, w_uk_t, num_branches: int) -> np.ndarray:
+    """Absorbed query of [MLRA] §1.3 step 1 ([MLA-LR] §3.3): for head i,
+    q~_i = W^UK_i^T q^N_i, so that q~_i . c = q^N_i . (W^UK_i c) for every latent
+    c. w_uk_t [h, d_c, d_h] stores W^UK_i^T (row n is the d_h-vector whose dot
+    with q^N_i gives q~_i[n]). Branch b takes q~_i[b*d_b:(b+1)*d_b] ([MLRA] §二).
+    Returns q_lat [B, h, n_b, d_b]."""
+    q_nope = np.asarray(q_nope, dtype=np.float64)
+    w = np.asarray(w_uk_t, dtype=np.float64)
+    B, h, dh = q_nope.shape
+    dc = w.shape[1]
+    q = np.einsum("ind,bid->bin", w, q_nope)                    # [B, h, d_c]
+    return q.reshape(B, h, num_branches, dc // num_branches)
+
+
+def prepare_decode(q_nope, q_pe, w_uk_t, num_branches, c_new, k_pe_new, positions, base=10000.0):
+    """The step before the attention call, for one new token per sequence at
+    position positions[b]: the absorbed query, the RoPE query rotated to that
+    position, and the token's cache row (its latent, then its RoPE key rotated to
+    the same position). Returns (q_lat, q_rope, row [B, d_c + d_R])."""
+    q_lat = absorb_query(q_nope, w_uk_t, num_branches)
+    q_rope = rope_rotate(q_pe, positions, base)
+    k_rot = rope_rotate(np.asarray(k_pe_new, dtype=np.float64), positions, base)
+    row = np.concatenate([np.asarray(c_new, dtype=np.float64), k_rot], axis=-1)
+    return q_lat, q_rope, row
 
 
 def shared_softmax_decode(q_lat, q_rope, kv_lat, kv_rope, seq_lens, w_v, sm_scale, alpha):

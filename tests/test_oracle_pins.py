@@ -14,6 +14,10 @@ mathematics fix, none of which re-types the oracle's own formula.
   paged gather                    page-table translation by hand-written indexing
   linearity                       alpha and W^V enter linearly
   planted mistakes                mutants of the oracle fail at least one pin
+  RoPE                            complex multiplication by exp(i m theta_j), relative-position
+                                  invariance of scores, frequencies, identity at position 0
+  query absorption                q~ . c == q^N . (W^UK c) for random latents c
+  prepare + decode                rotated cache and query == attention with the rotation in the score
 
 Page keys: [MLRA] "原生支持张量并行的多分支低秩注意力MLRA：优化KV缓存，实现2.8倍解码加速";
 [MLA-LR] "Multi-Head Latent Attention：低秩近似优化Transformer计算效率".
@@ -395,3 +399,99 @@ def test_bruteforce_on_tiny_f32_workload():
     args = (inp["q_lat"].double().numpy(), inp["q_rope"].double().numpy(), kv[:, :, :dc], kv[:, :, dc:],
             inp["seq_lens"].numpy(), inp["w_v"].double().numpy(), w.sm_scale, w.alpha)
     assert rel(O.mlra_decode_absorbed(*args), O.mlra_decode_bruteforce(*args)) < 1e-12
+
+
+# ---- the step before attention: RoPE rotation and query absorption ----------------------------
+
+def test_rope_rotation_is_complex_multiplication():
+    """Pair (x_2j, x_2j+1) at position m equals (x_2j + i x_2j+1) * exp(i m theta_j) with
+    theta_j = 10000^(-2j/d_R), computed here with numpy complex arithmetic."""
+    rng = np.random.default_rng(21)
+    dr, B = 8, 5
+    x = rng.standard_normal((B, 3, dr))
+    pos = np.array([0, 1, 7, 1000, 123457])
+    got = O.rope_rotate(x, pos)
+    theta = np.array([10000.0 ** (-2.0 * j / dr) for j in range(dr // 2)])
+    z = (x[..., 0::2] + 1j * x[..., 1::2]) * np.exp(1j * pos[:, None, None] * theta[None, None, :])
+    assert np.allclose(got[..., 0::2], z.real, atol=1e-12)
+    assert np.allclose(got[..., 1::2], z.imag, atol=1e-12)
+
+
+def test_rope_frequencies_and_identity():
+    ang = O.rope_angles([1], 32)[0]
+    assert ang[0] == 1.0 and math.isclose(ang[1], 10.0 ** -0.25, rel_tol=1e-14)
+    assert math.isclose(ang[15], 10000.0 ** (-30.0 / 32.0), rel_tol=1e-14)
+    x = np.random.default_rng(2).standard_normal((3, 2, 32))
+    assert np.array_equal(O.rope_rotate(x, [0, 0, 0]), x)
+
+
+def test_rope_scores_depend_on_relative_position_only():
+    """rot(q, m) . rot(k, n) depends on m - n alone, and each pair keeps its length."""
+    rng = np.random.default_rng(22)
+    q, k = rng.standard_normal((1, 16)), rng.standard_normal((1, 16))
+    def score(m, n):
+        return float(np.sum(O.rope_rotate(q, [m]) * O.rope_rotate(k, [n])))
+    for m, n in [(5, 2), (1003, 1000), (70000, 69997)]:
+        assert math.isclose(score(m, n), score(3, 0), rel_tol=1e-9, abs_tol=1e-9)
+    r = O.rope_rotate(q, [12345])
+    assert np.allclose(r[..., 0::2] ** 2 + r[..., 1::2] ** 2, q[..., 0::2] ** 2 + q[..., 1::2] ** 2)
+
+
+def test_absorbed_query_scores_like_the_up_projected_key():
+    """q~_i . c == q^N_i . (W^UK_i c) for random latents c (a transposed W fails this)."""
+    rng = np.random.default_rng(23)
+    B, h, dh, nb, db = 2, 3, 12, 4, 2
+    dc = nb * db
+    q_nope = rng.standard_normal((B, h, dh))
+    w = rng.standard_normal((h, dh, dc))                 # W^UK_i: latent -> key
+    q_lat = O.absorb_query(q_nope, np.transpose(w, (0, 2, 1)), nb)
+    assert q_lat.shape == (B, h, nb, db)
+    c = rng.standard_normal((4, dc))
+    for b in range(B):
+        for i in range(h):
+            lhs = q_lat[b, i].reshape(dc) @ c.T
+            rhs = q_nope[b, i] @ (w[i] @ c.T)
+            assert np.allclose(lhs, rhs, rtol=1e-12, atol=1e-12)
+
+
+def test_prepared_decode_equals_attention_on_rotated_keys():
+    """End to end: keys stored rotated by the prepare step, the query rotated to its own
+    position, then decoded, equals attention written directly on un-rotated keys with
+    the rotation applied inside each score (materialised per-branch keys)."""
+    rng = np.random.default_rng(24)
+    B, h, nb, db, dr, dh = 2, 2, 2, 4, 6, 8
+    dc = nb * db
+    L = 9
+    c_all = rng.standard_normal((B, L, dc))
+    kpe_raw = rng.standard_normal((B, L, dr))
+    q_nope = rng.standard_normal((B, h, dh))
+    q_pe = rng.standard_normal((B, h, dr))
+    w = rng.standard_normal((h, dh, dc)) / 3.0
+    w_v = rng.standard_normal((h, dh, dc)) / 3.0
+    pos = np.array([L - 1, L - 1])
+    # cache rows 0 .. L-2 already rotated; the prepare step writes row L-1
+    kv = np.zeros((B, L, dc + dr))
+    for s in range(L - 1):
+        kv[:, s, :dc] = c_all[:, s]
+        kv[:, s, dc:] = O.rope_rotate(kpe_raw[:, s], [s, s])
+    q_lat, q_rope, row = O.prepare_decode(q_nope, q_pe, np.transpose(w, (0, 2, 1)), nb,
+                                          c_all[:, L - 1], kpe_raw[:, L - 1], pos)
+    kv[:, L - 1] = row
+    lens = np.array([L, L])
+    y = O.mlra_decode_absorbed(q_lat, q_rope, kv[:, :, :dc], kv[:, :, dc:], lens, w_v, 0.3, 0.5)
+    ref = np.zeros((B, h, dh))
+    for b in range(B):
+        for i in range(h):
+            for br in range(nb):
+                sl = slice(br * db, (br + 1) * db)
+                z = np.empty(L)
+                for s in range(L):
+                    k_nope = w[i][:, sl] @ c_all[b, s, sl]                     # materialised key
+                    qr = O.rope_rotate(q_pe[b:b + 1, i], [L - 1])[0]
+                    kr = O.rope_rotate(kpe_raw[b:b + 1, s], [s])[0]
+                    z[s] = 0.3 * (q_nope[b, i] @ k_nope + qr @ kr)
+                p = np.exp(z - z.max())
+                p /= p.sum()
+                u = p @ c_all[b, :, sl]
+                ref[b, i] += w_v[i][:, sl] @ u
+    assert np.allclose(y, 0.5 * ref, rtol=1e-10, atol=1e-12)
