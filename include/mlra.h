@@ -171,6 +171,74 @@ mlra_status mlra_decode(const mlra_decode_args* args, void* stream);
 mlra_status mla_decode(const mlra_decode_args* args, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * The step before a decode call, for one new token per sequence:
+ *  - query absorption, [MLRA] §1.3 step 1 (and §二 for the branch split):
+ *      q~_i = W^UK_i^T q^N_i,  q_lat[beta][i][b][:] = q~_i[b*d_b:(b+1)*d_b];
+ *  - the RoPE query rotated to the new token's position m;
+ *  - the new token's cache row: its latent, and its RoPE key rotated to m.
+ * Rotation at position m ([DS-MLA] decoupled RoPE; the pages print no formula,
+ * the original rotary form is taken): consecutive pairs (x_2j, x_2j+1) become
+ *   (x_2j cos a - x_2j+1 sin a, x_2j sin a + x_2j+1 cos a),  a = m * rope_base^(-2j/d_R).
+ * The angle and its sine and cosine are computed in fp64, the rotation in fp32.
+ *
+ * Shapes (all contiguous, type dtype):
+ *   q_nope   [B][h][d_h]    NoPE query of each head, before absorption
+ *   q_pe     [B][h][d_R]    RoPE query, before rotation (d_R even, at most 256)
+ *   w_uk     [h][d_c][d_h]  W^UK_i transposed: row n of head i is the d_h-vector
+ *                           whose dot with q^N_i gives q~_i[n] (W^UK_i maps a
+ *                           latent to the head's NoPE key)
+ *   c_new    [B][d_c]       latent of the new token
+ *   k_pe_new [B][d_R]       RoPE key of the new token, before rotation
+ *   positions device int32 [B]: the new token's position m, which is also its row
+ *            in the cache; the decode that follows uses seq_lens = positions + 1.
+ *   positions_host optional host copy, validated (0 <= m, m < max_seq_len when
+ *            contiguous, m < max_pages*page_size when paged).
+ *   q_lat, q_rope  outputs in the layout mlra_decode takes.
+ *   kv_lat, kv_rope, row_stride, seq_stride, max_seq_len, page_size, page_table,
+ *   max_pages, num_pages: the cache, addressed exactly as in mlra_decode_args.
+ *   The latent is copied bit-exactly; the rotated RoPE key is rounded once to dtype.
+ * Errors: host validation as for mlra_decode. On the device, a position outside
+ * the cache sets MLRA_FLAG_SEQ_LEN_CLAMPED and a page-table entry outside
+ * [0, num_pages) sets MLRA_FLAG_BAD_PAGE in *error_flags; that sequence's row is
+ * then not written (its queries still are).
+ * The bf16 path uses MFMAs for the absorption when d_h % 32 == 0, d_h <= 256,
+ * d_c % 16 == 0 and q_nope, w_uk are 16-byte aligned; other shapes and fp32 use
+ * the vector ALUs.
+ * ------------------------------------------------------------------------- */
+typedef struct mlra_prepare_args {
+  int32_t batch;
+  int32_t num_heads;
+  int32_t num_branches;
+  int32_t branch_dim;
+  int32_t rope_dim;
+  int32_t head_dim;
+  int32_t dtype;
+  float rope_base;
+  const void* q_nope;
+  const void* q_pe;
+  const void* w_uk;
+  const void* c_new;
+  const void* k_pe_new;
+  const int32_t* positions;
+  const int32_t* positions_host;
+  void* q_lat;
+  void* q_rope;
+  void* kv_lat;
+  void* kv_rope;
+  int64_t row_stride;
+  int64_t seq_stride;
+  int32_t max_seq_len;
+  int32_t page_size;
+  const int32_t* page_table;
+  int32_t max_pages;
+  int32_t num_pages;
+  uint32_t* error_flags;
+} mlra_prepare_args;
+
+/* Enqueue the step above (one kernel) on `stream`. */
+mlra_status mlra_decode_prepare(const mlra_prepare_args* args, void* stream);
+
+/* ---------------------------------------------------------------------------
  * Paged cache. A pool is `num_pages` pages of `page_size` rows of `row_stride`
  * elements; a page table maps a sequence's logical page j to a physical page.
  * ------------------------------------------------------------------------- */

@@ -32,6 +32,7 @@ EXPORTED_SYMBOLS = (
     "mlra_last_error", "mlra_version", "mlra_decode_workspace_size", "mlra_decode_validate", "mlra_decode",
     "mla_decode", "mlra_paged_append", "mlra_paged_gather", "mlra_page_table_check", "mlra_page_pool_create",
     "mlra_page_pool_alloc", "mlra_page_pool_free", "mlra_page_pool_num_free", "mlra_page_pool_destroy",
+    "mlra_decode_prepare",
 )
 
 
@@ -60,6 +61,23 @@ class DecodeArgs(ctypes.Structure):
     ]
 
 
+class PrepareArgs(ctypes.Structure):
+    """Mirror of ``mlra_prepare_args`` (include/mlra.h)."""
+    _fields_ = [
+        ("batch", ctypes.c_int32), ("num_heads", ctypes.c_int32), ("num_branches", ctypes.c_int32),
+        ("branch_dim", ctypes.c_int32), ("rope_dim", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+        ("dtype", ctypes.c_int32), ("rope_base", ctypes.c_float),
+        ("q_nope", ctypes.c_void_p), ("q_pe", ctypes.c_void_p), ("w_uk", ctypes.c_void_p),
+        ("c_new", ctypes.c_void_p), ("k_pe_new", ctypes.c_void_p),
+        ("positions", ctypes.c_void_p), ("positions_host", ctypes.c_void_p),
+        ("q_lat", ctypes.c_void_p), ("q_rope", ctypes.c_void_p),
+        ("kv_lat", ctypes.c_void_p), ("kv_rope", ctypes.c_void_p),
+        ("row_stride", ctypes.c_int64), ("seq_stride", ctypes.c_int64), ("max_seq_len", ctypes.c_int32),
+        ("page_size", ctypes.c_int32), ("page_table", ctypes.c_void_p), ("max_pages", ctypes.c_int32),
+        ("num_pages", ctypes.c_int32), ("error_flags", ctypes.c_void_p),
+    ]
+
+
 _lib = None
 
 
@@ -79,6 +97,7 @@ def lib() -> ctypes.CDLL:
         L.mlra_decode_validate.argtypes = [P(DecodeArgs)]
         L.mlra_decode.argtypes = [P(DecodeArgs), vp]
         L.mla_decode.argtypes = [P(DecodeArgs), vp]
+        L.mlra_decode_prepare.argtypes = [P(PrepareArgs), vp]
         L.mlra_paged_append.argtypes = [vp, i64, i32, i32, i32, vp, i32, vp, vp, i32, i32, vp, vp]
         L.mlra_paged_gather.argtypes = [vp, i64, i32, i32, i32, vp, i32, vp, i32, i32, i32, vp, vp, vp]
         L.mlra_page_table_check.argtypes = [vp, i32, i32, vp, i32, i32]
@@ -89,7 +108,7 @@ def lib() -> ctypes.CDLL:
         L.mlra_page_pool_num_free.restype = i32
         L.mlra_page_pool_destroy.argtypes = [vp]
         L.mlra_page_pool_destroy.restype = None
-        for name in ("mlra_decode_validate", "mlra_decode", "mla_decode", "mlra_paged_append",
+        for name in ("mlra_decode_validate", "mlra_decode", "mla_decode", "mlra_decode_prepare", "mlra_paged_append",
                      "mlra_paged_gather", "mlra_page_table_check", "mlra_page_pool_create",
                      "mlra_page_pool_alloc", "mlra_page_pool_free"):
             getattr(L, name).restype = i32
@@ -213,6 +232,53 @@ def mla_decode(q_lat, q_rope, kv_lat, kv_rope, seq_lens, w_v, *, sm_scale: float
     if q_lat.dim() == 3:
         q_lat = q_lat.unsqueeze(2)
     return _run("mla_decode", q_lat, q_rope, kv_lat, kv_rope, seq_lens, w_v, sm_scale=sm_scale, alpha=alpha, **kw)
+
+
+def make_prepare_args(q_nope, q_pe, w_uk_t, c_new, k_pe_new, positions, kv_lat, kv_rope, *, num_branches: int,
+                      q_lat: torch.Tensor, q_rope: torch.Tensor, rope_base: float = 10000.0,
+                      positions_host: Optional[torch.Tensor] = None, row_stride: Optional[int] = None,
+                      seq_stride: Optional[int] = None, max_seq_len: Optional[int] = None,
+                      page_table: Optional[torch.Tensor] = None, page_size: int = 64, num_pages: int = 0,
+                      error_flags: Optional[torch.Tensor] = None) -> PrepareArgs:
+    """Fill ``mlra_prepare_args`` (shapes as in include/mlra.h; w_uk_t is [h, d_c, d_h])."""
+    B, H, DH = q_nope.shape
+    DC = w_uk_t.shape[1]
+    a = PrepareArgs()
+    a.batch, a.num_heads, a.num_branches = B, H, num_branches
+    a.branch_dim, a.rope_dim, a.head_dim = DC // num_branches, q_pe.shape[-1], DH
+    a.dtype = _dtype_code(q_nope.dtype)
+    a.rope_base = float(rope_base)
+    a.q_nope, a.q_pe, a.w_uk = _ptr(q_nope), _ptr(q_pe), _ptr(w_uk_t)
+    a.c_new, a.k_pe_new, a.positions = _ptr(c_new), _ptr(k_pe_new), _ptr(positions)
+    if positions_host is not None:
+        assert positions_host.device.type == "cpu" and positions_host.dtype == torch.int32
+        a.positions_host = positions_host.data_ptr()
+    a.q_lat, a.q_rope = _ptr(q_lat), _ptr(q_rope)
+    a.kv_lat, a.kv_rope = _ptr(kv_lat), _ptr(kv_rope)
+    a.row_stride = int(row_stride if row_stride is not None else kv_lat.stride(-2))
+    if page_table is None:
+        a.seq_stride = int(seq_stride if seq_stride is not None else kv_lat.stride(0))
+        a.max_seq_len = int(max_seq_len if max_seq_len is not None else kv_lat.shape[-2])
+    else:
+        a.page_table, a.max_pages, a.page_size, a.num_pages = _ptr(page_table), page_table.shape[1], page_size, num_pages
+    a.error_flags = _ptr(error_flags)
+    return a
+
+
+def prepare(q_nope, q_pe, w_uk_t, c_new, k_pe_new, positions, kv_lat, kv_rope, *, num_branches: int,
+            q_lat: Optional[torch.Tensor] = None, q_rope: Optional[torch.Tensor] = None, stream=None, **kw):
+    """The step before a decode call: absorbed query, rotated RoPE query, new cache row.
+    Returns (q_lat [B, h, n_b, d_b], q_rope [B, h, d_R])."""
+    B, H, _ = q_nope.shape
+    DC = w_uk_t.shape[1]
+    if q_lat is None:
+        q_lat = torch.empty((B, H, num_branches, DC // num_branches), dtype=q_nope.dtype, device=q_nope.device)
+    if q_rope is None:
+        q_rope = torch.empty_like(q_pe)
+    args = make_prepare_args(q_nope, q_pe, w_uk_t, c_new, k_pe_new, positions, kv_lat, kv_rope,
+                             num_branches=num_branches, q_lat=q_lat, q_rope=q_rope, **kw)
+    _check(lib().mlra_decode_prepare(ctypes.byref(args), _stream_handle(stream)))
+    return q_lat, q_rope
 
 
 def split_rows(kv: torch.Tensor, latent_dim: int):

@@ -303,6 +303,73 @@ mlra_status mla_decode(const mlra_decode_args* args, void* stream) {
   return run_decode(args, stream);
 }
 
+mlra_status mlra_decode_prepare(const mlra_prepare_args* a, void* stream) {
+  if (!a) return fail(MLRA_ERR_INVALID_ARG, "args is NULL");
+  if (a->batch < 1 || a->num_heads < 1 || a->num_branches < 1 || a->branch_dim < 1 || a->head_dim < 1)
+    return fail(MLRA_ERR_INVALID_ARG, "batch, num_heads, num_branches, branch_dim and head_dim must be >= 1");
+  if (a->rope_dim < 0 || a->rope_dim % 2 || a->rope_dim > 256)
+    return fail(MLRA_ERR_INVALID_ARG, "rope_dim must be even, >= 0 and <= 256 (got %d)", a->rope_dim);
+  if (a->dtype != MLRA_BF16 && a->dtype != MLRA_F32) return fail(MLRA_ERR_INVALID_ARG, "dtype %d is not a mlra_dtype", a->dtype);
+  if (!std::isfinite(a->rope_base) || !(a->rope_base > 0.f))
+    return fail(MLRA_ERR_INVALID_ARG, "rope_base must be finite and > 0");
+  if (!a->q_nope || !a->q_pe || !a->w_uk || !a->c_new || !a->k_pe_new || !a->positions || !a->q_lat || !a->q_rope ||
+      !a->kv_lat || !a->kv_rope)
+    return fail(MLRA_ERR_INVALID_ARG, "a required pointer is NULL");
+  if (a->row_stride < 1) return fail(MLRA_ERR_INVALID_ARG, "row_stride must be >= 1");
+  const bool paged = a->page_table != nullptr;
+  int64_t capacity;
+  if (paged) {
+    if (!is_pow2(a->page_size)) return fail(MLRA_ERR_INVALID_ARG, "page_size must be a power of two (got %d)", a->page_size);
+    if (a->num_pages < 1 || a->max_pages < 1) return fail(MLRA_ERR_INVALID_ARG, "num_pages and max_pages must be >= 1");
+    capacity = (int64_t)a->max_pages * a->page_size;
+  } else {
+    if (a->max_seq_len < 1) return fail(MLRA_ERR_INVALID_ARG, "max_seq_len must be >= 1");
+    if (a->batch > 1 && a->seq_stride < (int64_t)(a->max_seq_len - 1) * a->row_stride + 1)
+      return fail(MLRA_ERR_INVALID_ARG, "seq_stride is smaller than max_seq_len rows");
+    capacity = a->max_seq_len;
+  }
+  if (a->positions_host) {
+    for (int i = 0; i < a->batch; ++i)
+      if (a->positions_host[i] < 0 || a->positions_host[i] >= capacity)
+        return fail(MLRA_ERR_INVALID_ARG, "positions[%d] = %d is outside the cache (capacity %lld)", i,
+                    a->positions_host[i], (long long)capacity);
+  }
+  const int64_t dc = (int64_t)a->num_branches * a->branch_dim;
+  const int64_t eb = a->dtype == MLRA_BF16 ? 2 : 4;
+  mlra::PrepareParams p{};
+  p.B = a->batch;
+  p.H = a->num_heads;
+  p.NB = a->num_branches;
+  p.DB = a->branch_dim;
+  p.DR = a->rope_dim;
+  p.DH = a->head_dim;
+  p.dtype = a->dtype;
+  p.mfma = a->dtype == MLRA_BF16 && mlra::prepare_mfma_supported(a->head_dim, (int)dc) && aligned(a->q_nope, 16) &&
+           aligned(a->w_uk, 16);
+  p.rope_base = a->rope_base;
+  p.q_nope = a->q_nope;
+  p.q_pe = a->q_pe;
+  p.w_uk = a->w_uk;
+  p.c_new = a->c_new;
+  p.k_pe_new = a->k_pe_new;
+  p.positions = a->positions;
+  p.q_lat = a->q_lat;
+  p.q_rope = a->q_rope;
+  p.kv_lat = a->kv_lat;
+  p.kv_rope = a->kv_rope;
+  p.row_stride_b = a->row_stride * eb;
+  p.seq_stride_b = a->seq_stride * eb;
+  p.max_seq_len = a->max_seq_len;
+  p.page_shift = paged ? ilog2(a->page_size) : 0;
+  p.page_table = a->page_table;
+  p.max_pages = a->max_pages;
+  p.num_pages = a->num_pages;
+  p.error_flags = a->error_flags;
+  hipError_t e = mlra::launch_prepare(p, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "prepare kernel launch");
+  return ok();
+}
+
 mlra_status mlra_paged_append(void* pool, int64_t row_stride, int32_t row_elems, int32_t page_size, int32_t num_pages,
                               const int32_t* page_table, int32_t max_pages, const int32_t* positions, const void* rows,
                               int32_t batch, int32_t dtype, uint32_t* error_flags, void* stream) {

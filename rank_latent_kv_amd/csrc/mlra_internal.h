@@ -74,6 +74,34 @@ size_t merge_lds_bytes(int nb, int db, int num_splits);
 constexpr size_t kMergeLdsLimit = 60 * 1024;
 hipError_t launch_merge(const MergeParams& p, hipStream_t stream);
 
+// The step before a decode call: query absorption, RoPE rotation, new cache rows.
+struct PrepareParams {
+  int B, H, NB, DB, DR, DH;
+  int dtype;                 // 0 bf16, 1 f32
+  bool mfma;                 // bf16 with d_h % 32 == 0, d_c % 16 == 0 and 16-byte aligned operands
+  float rope_base;
+  const void* q_nope;
+  const void* q_pe;
+  const void* w_uk;
+  const void* c_new;
+  const void* k_pe_new;
+  const int32_t* positions;
+  void* q_lat;
+  void* q_rope;
+  void* kv_lat;
+  void* kv_rope;
+  int64_t row_stride_b;
+  int64_t seq_stride_b;
+  int max_seq_len;
+  int page_shift;
+  const int32_t* page_table;
+  int max_pages;
+  int num_pages;
+  uint32_t* error_flags;
+};
+bool prepare_mfma_supported(int dh, int dc);
+hipError_t launch_prepare(const PrepareParams& p, hipStream_t stream);
+
 // Paged cache copies.
 hipError_t launch_paged_append(void* pool, int64_t row_stride, int32_t row_elems, int32_t page_size,
                                int32_t num_pages, const int32_t* page_table, int32_t max_pages,

@@ -330,3 +330,51 @@ def test_auto_split_fits_one_pass_over_the_cus():
     groups = sum(-(-L // (-(-split_tokens // 128) * 128)) for L in lens)
     assert splits == -(-max(lens) // 1792)
     assert groups <= 256
+
+
+# ---- the prepare step ------------------------------------------------------------------------
+
+def test_prepare_struct_layout_matches_header():
+    fields = [f[0] for f in R.PrepareArgs._fields_]
+    src = ["#include <stdio.h>", "#include <stddef.h>", '#include "mlra.h"', "int main(void) {",
+           'printf("size %zu\\n", sizeof(mlra_prepare_args));']
+    src += [f'printf("{f} %zu\\n", offsetof(mlra_prepare_args, {f}));' for f in fields]
+    src += ["return 0; }"]
+    with tempfile.TemporaryDirectory() as d:
+        c = os.path.join(d, "layout.c")
+        exe = os.path.join(d, "layout")
+        open(c, "w").write("\n".join(src))
+        subprocess.run(["gcc", "-std=c99", "-I", os.path.join(ROOT, "include"), c, "-o", exe], check=True)
+        got = dict(line.split() for line in subprocess.run([exe], capture_output=True, text=True).stdout.splitlines())
+    assert int(got["size"]) == ctypes.sizeof(R.PrepareArgs)
+    for f in fields:
+        assert int(got[f]) == getattr(R.PrepareArgs, f).offset, f
+
+
+def prepare_args(**over):
+    a = R.PrepareArgs()
+    a.batch, a.num_heads, a.num_branches, a.branch_dim, a.rope_dim, a.head_dim = 2, 64, 4, 32, 32, 128
+    a.dtype, a.rope_base = R.MLRA_BF16, 10000.0
+    for name in ("q_nope", "q_pe", "w_uk", "c_new", "k_pe_new", "positions", "q_lat", "q_rope", "kv_lat"):
+        setattr(a, name, FAKE)
+    a.kv_rope = FAKE + 256
+    a.row_stride, a.seq_stride, a.max_seq_len = 160, 160 * 100, 100
+    for k, v in over.items():
+        setattr(a, k, v)
+    return a
+
+
+@pytest.mark.parametrize("field,value", [("rope_dim", 31), ("dtype", 5), ("rope_base", 0.0), ("batch", 0),
+                                         ("q_nope", None), ("kv_lat", None), ("max_seq_len", 0), ("row_stride", 0)])
+def test_prepare_rejects_bad_arguments(field, value):
+    """Host validation fails before any HIP call (no GPU needed)."""
+    a = prepare_args(**{field: value})
+    assert R.lib().mlra_decode_prepare(ctypes.byref(a), None) == R.MLRA_ERR_INVALID_ARG
+    assert R.last_error() != ""
+
+
+def test_prepare_rejects_positions_outside_the_cache():
+    pos = (ctypes.c_int32 * 2)(5, 100)
+    a = prepare_args(positions_host=ctypes.cast(pos, ctypes.c_void_p).value)
+    assert R.lib().mlra_decode_prepare(ctypes.byref(a), None) == R.MLRA_ERR_INVALID_ARG
+    assert "outside the cache" in R.last_error()
