@@ -10,13 +10,15 @@
 // by all branches).
 //
 // Work split inside the group. A "unit" is (branch b, group of 32 heads). Each wave owns
-// one branch and some head groups, and possibly only every P-th 32-token sub-tile (a
-// "phase"); phases are merged in LDS at the end.
+// BPW branches (a branch group) and some head groups, and possibly only every P-th 32-token
+// sub-tile (a "phase"); phases are merged in LDS at the end.
 //
 // Per 32-token sub-tile and unit:
 //   scores  S^T[tok x head] = C_ext[tok x (d_R+d_b)] . Q_ext^T, MFMA with the exact bf16
-//           query and fp32 accumulation; the logit in log2 units is x = S * tau*log2(e)
-//           minus the reference max, one fma;
+//           query and fp32 accumulation. The RoPE part q^R . k^R does not depend on the
+//           branch: with two branches per wave it is computed once and seeds both
+//           branches' latent chains. The logit in log2 units is x = S * tau*log2(e) minus
+//           the reference max, one fma;
 //   softmax lazy running max: the reference m is the exact max of the split's first
 //           sub-tile and only moves (with a rescale of O and l) when a sub-tile's
 //           weights sum past 2^16; p = 2^(x-m) is packed to bf16 and l accumulates the
@@ -24,7 +26,8 @@
 //           the P.C product uses;
 //   values  O^T[feat x head] += C_b^T[feat x tok] . P^T[tok x head], MFMA, with the
 //           transposed latent read by ds_read_b64_tr_b16.
-// The score MFMAs of the next sub-tile are issued before the softmax of the current one.
+// With one branch per wave, the score MFMAs of the next sub-tile are issued before the
+// softmax of the current one.
 // Each split writes its unnormalised (o, m, l); the merge kernel combines the splits
 // (log-sum-exp) and applies W^V per branch.
 #include <hip/hip_runtime.h>
@@ -56,21 +59,29 @@ constexpr int kPageCache = 256;            // page ids of one split kept in LDS 
 constexpr float kRescaleThreshold = 8.0f;  // log2 units: p = 2^x stays <= 256
 constexpr float kStageSumMax = 65536.0f;   // a lane's sub-tile weights summing past this trigger the exact max
 
-template <int NB, int DB, int DR, int HEADS, int W, bool PAGED>
+template <int NB, int DB, int DR, int HEADS, int W, bool PAGED, int BPW>
 struct Cfg {
   static constexpr int WAVES = W;                        // waves per work-group
   static constexpr int THREADS = W * 64;
   static constexpr int NHG = (HEADS + 31) / 32;          // head groups (MFMA N = 32)
-  static constexpr int WPB = W / NB;                     // waves per branch
-  static constexpr int HGSPLIT = WPB < NHG ? WPB : NHG;  // head-group slots per branch
+  static constexpr int NBG = NB / BPW;                   // branch groups (BPW branches per wave)
+  static constexpr int WPB = W / NBG;                    // waves per branch group
+  static constexpr int HGSPLIT = WPB < NHG ? WPB : NHG;  // head-group slots per branch group
   static constexpr int HPW = NHG / HGSPLIT;              // head groups per wave
   static constexpr int P = WPB / HGSPLIT;                // token phases
   static constexpr int SUB = P > MLRA_SUB_PREF ? P : MLRA_SUB_PREF;   // 32-token sub-tiles per stage
   static constexpr int NSW = SUB / P;                    // sub-tiles of one wave per stage
+  // one branch per wave: the next sub-tile's scores are issued before the current softmax;
+  // with several branches per wave their score tiles leave no registers for that
+  static constexpr bool PIPE = BPW == 1;
   static constexpr int ST = 32 * SUB;                    // tokens per stage
   static constexpr int NCL = NB * DB / 8;                // latent 16-byte chunks per row
   static constexpr int NCR = DR / 8;                     // RoPE 16-byte chunks per row
   static constexpr int NCH = NCL + NCR;
+  // Latent chunks never wrap around their LDS row (largest latent chunk + largest rotation
+  // < NCH): their per-lane offsets are then one base plus compile-time constants.
+  static constexpr int MAXROT = NCH % 8 == 0 ? 7 : 3;
+  static constexpr bool LAT_FLAT = NCL - 1 + MAXROT < NCH;
   static constexpr int SUB_BYTES = 32 * NCH * 16;
   static constexpr int STAGE_BYTES = ST * NCH * 16;
   static constexpr int DMA_PER_STAGE = ST * NCH / 64;    // wave-wide 1 KiB DMA instructions
@@ -81,15 +92,16 @@ struct Cfg {
   static constexpr int MT = DB / 32;                     // value M-tiles (32 features)
   static constexpr int KR = DR / 16;                     // RoPE K-chunks of the score
   static constexpr int KL = DB / 16;                     // latent K-chunks of the score
-  static constexpr int MERGE_WAVES = W - NB * HGSPLIT;
-  static constexpr int MERGE_FLOATS = HPW * (16 * MT + 2) * 64;   // per wave record
+  static constexpr int MERGE_WAVES = W - NBG * HGSPLIT;
+  static constexpr int MERGE_FLOATS = HPW * BPW * (16 * MT + 2) * 64;   // per wave record
   static constexpr int PTAB_BYTES = PAGED ? kPageCache * 4 : 0;
   static constexpr int NS_FIT = (kLdsBytes - PTAB_BYTES) / STAGE_BYTES;
   static constexpr int NS = NS_FIT < kMaxStages ? NS_FIT : kMaxStages;   // ring depth
   static constexpr int RING_BYTES = NS * STAGE_BYTES;
   static constexpr int MERGE_BYTES = MERGE_WAVES * MERGE_FLOATS * 4;
   static constexpr int LDS_BYTES = (RING_BYTES > MERGE_BYTES ? RING_BYTES : MERGE_BYTES) + PTAB_BYTES;
-  static_assert(W % NB == 0, "branches must divide the waves");
+  static_assert(NB % BPW == 0, "branches per wave must divide the branches");
+  static_assert(W % NBG == 0, "branch groups must divide the waves");
   static_assert(NHG % HGSPLIT == 0, "head groups must split evenly");
   static_assert(SUB % P == 0, "phases must divide the sub-tiles");
   static_assert(DB % 32 == 0 && DR % 16 == 0, "MFMA tiling");
@@ -154,18 +166,25 @@ __device__ __forceinline__ void wait_dma(int ahead) {
 
 __device__ __forceinline__ void block_barrier() { asm volatile("s_barrier" : : : "memory"); }
 
-__device__ __forceinline__ float other_half(float x) {
-  // value held by lane l ^ 32 (the lane holding the other 16 tokens of a head)
-  return __shfl_xor(x, 32, 64);
+// Max and sum of the values held by lanes l and l ^ 32 (the two lanes holding the two
+// 16-token halves of one head's column). v_permlane32_swap with the same register as both
+// operands leaves x[l] in one result and x[l ^ 32] in the other, in every lane.
+__device__ __forceinline__ float halves_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float halves_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 __device__ __forceinline__ bf16x8 load_q8(const __bf16* src) {
   return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(src));
 }
 
-template <int NB, int DB, int DR, int HEADS, int W, bool PAGED>
+template <int NB, int DB, int DR, int HEADS, int W, bool PAGED, int BPW>
 __global__ __launch_bounds__(W * 64, 1) void attn_mfma_kernel(AttnParams p) {
-  using C = Cfg<NB, DB, DR, HEADS, W, PAGED>;
+  using C = Cfg<NB, DB, DR, HEADS, W, PAGED, BPW>;
   __shared__ __attribute__((aligned(1024))) char smem[C::LDS_BYTES];
   int* ptab = reinterpret_cast<int*>(smem + C::LDS_BYTES - C::PTAB_BYTES);
 
@@ -184,7 +203,7 @@ __global__ __launch_bounds__(W * 64, 1) void attn_mfma_kernel(AttnParams p) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int b = wave / C::WPB;
+  const int bg = wave / C::WPB;     // branch group: branches bg * BPW ... bg * BPW + BPW - 1
   const int wr = wave % C::WPB;
   const int hgslot = wr % C::HGSPLIT;
   const int phase = wr / C::HGSPLIT;
@@ -217,8 +236,8 @@ __global__ __launch_bounds__(W * 64, 1) void attn_mfma_kernel(AttnParams p) {
     int tok;
     int chunk;
   };
-  auto dma_lane = [&](int i) __attribute__((always_inline)) -> DmaLane {
-    const int f = min(wave + C::DW * i, C::DMA_PER_STAGE - 1) * 64 + lane;
+  auto dma_lane = [&](int i, int ln) __attribute__((always_inline)) -> DmaLane {
+    const int f = min(wave + C::DW * i, C::DMA_PER_STAGE - 1) * 64 + ln;
     const int t = f / C::NCH;
     int c = f - t * C::NCH - chunk_rot<C::NCH>(t);
     if (c < 0) c += C::NCH;
@@ -240,7 +259,7 @@ __global__ __launch_bounds__(W * 64, 1) void attn_mfma_kernel(AttnParams p) {
   int pslot[C::DMA_HI];
 #pragma unroll
   for (int i = 0; i < C::DMA_HI; ++i) {
-    const DmaLane d = dma_lane(i);
+    const DmaLane d = dma_lane(i, lane);
     const char* sel = chunk_src(d.chunk);
     if constexpr (PAGED) {
       const int rin = big_pages ? d.tok : (d.tok & pmask);
@@ -279,20 +298,27 @@ __global__ __launch_bounds__(W * 64, 1) void attn_mfma_kernel(AttnParams p) {
         dma16(src, __builtin_amdgcn_readfirstlane(ring + (uint32_t)((wave + C::DW * i) * 1024)));
       }
     } else {
-      // ragged last stage: rows past the end repeat the last row (finite data, masked later)
+      // ragged last stage: rows past the end repeat the last row (finite data, masked later).
+      // The source is the lane's full-stage pointer moved to the wanted row, and the lane's
+      // token is recomputed here from an opaque copy of the lane index, so that nothing of
+      // this once-per-split path stays live (or spills) through the main loop.
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
 #pragma unroll
       for (int i = 0; i < C::DMA_HI; ++i) {
         if (i >= ndma) break;
-        const DmaLane d = dma_lane(i);
+        const DmaLane d = dma_lane(i, ln);
         const int tok = min(tok0 + d.tok, t1 - 1);
-        int64_t row;
+        int64_t row, row_of_dptr;
         if constexpr (PAGED) {
           const int pg = ptab[(tok >> p.page_shift) - first_page];
           row = ((int64_t)pg << p.page_shift) | (tok & pmask);
+          row_of_dptr = big_pages ? d.tok : (d.tok & pmask);
         } else {
           row = tok;
+          row_of_dptr = t0 + d.tok;
         }
-        const char* src = chunk_src(d.chunk) + row * p.row_stride_b;
+        const char* src = dptr[i] + (row - row_of_dptr) * p.row_stride_b;
         dma16(src, __builtin_amdgcn_readfirstlane(ring + (uint32_t)((wave + C::DW * i) * 1024)));
       }
     }
@@ -300,78 +326,110 @@ __global__ __launch_bounds__(W * 64, 1) void attn_mfma_kernel(AttnParams p) {
 
   // ---- queries: B operands (exact bf16 values) ---------------------------------------------
   bf16x8 qr[C::HPW][C::KR];
-  bf16x8 ql[C::HPW][C::KL];
+  bf16x8 ql[C::HPW][BPW][C::KL];
 #pragma unroll
   for (int h = 0; h < C::HPW; ++h) {
     const int head = (hgslot * C::HPW + h) * 32 + n32;
     const bool live = head < p.H;
     const __bf16* qrp = reinterpret_cast<const __bf16*>(p.q_rope) + ((int64_t)beta * p.H + head) * DR;
-    const __bf16* qlp =
-        reinterpret_cast<const __bf16*>(p.q_lat) + (((int64_t)beta * p.H + head) * NB + b) * DB;
 #pragma unroll
     for (int k = 0; k < C::KR; ++k) qr[h][k] = live ? load_q8(qrp + 16 * k + 8 * g) : bf16x8{};
 #pragma unroll
-    for (int k = 0; k < C::KL; ++k) ql[h][k] = live ? load_q8(qlp + 16 * k + 8 * g) : bf16x8{};
+    for (int bb = 0; bb < BPW; ++bb) {
+      const __bf16* qlp =
+          reinterpret_cast<const __bf16*>(p.q_lat) + (((int64_t)beta * p.H + head) * NB + bg * BPW + bb) * DB;
+#pragma unroll
+      for (int k = 0; k < C::KL; ++k) ql[h][bb][k] = live ? load_q8(qlp + 16 * k + 8 * g) : bf16x8{};
+    }
   }
 
   // ---- per-lane LDS offsets inside a sub-tile -------------------------------------------
-  int off_r[C::KR], off_l[C::KL], off_v[C::MT][2];
+  int off_r[C::KR], off_l[BPW][C::KL], off_v[BPW][C::MT][2];
 #pragma unroll
   for (int k = 0; k < C::KR; ++k) off_r[k] = lds_chunk_offset<C::NCH>(n32, C::NCL + 2 * k + g);
-#pragma unroll
-  for (int k = 0; k < C::KL; ++k) off_l[k] = lds_chunk_offset<C::NCH>(n32, b * (DB / 8) + 2 * k + g);
   {
     const int q4 = lane >> 4, jj = lane & 15;
-    const int tt = 4 * (q4 >> 1) + (jj >> 2);                       // token within an 8-token half
+    const int tt = 4 * (q4 >> 1) + (jj >> 2);                        // token within an 8-token half
+    // score operand: chunk 2k + g of branch br for token n32; value operand: the 8-byte word
+    // of feature f for tokens tt and tt + 8 (whose rotation is 2 larger)
+    const int lat0 = lds_chunk_offset<C::NCH>(n32, bg * BPW * (DB / 8) + g);
+    const int f0 = bg * BPW * DB + 16 * (q4 & 1) + 4 * (jj & 3);
+    const int val0 = lds_chunk_offset<C::NCH>(tt, f0 >> 3) + (f0 & 7) * 2;
 #pragma unroll
-    for (int mt = 0; mt < C::MT; ++mt) {
-      const int f = b * DB + 32 * mt + 16 * (q4 & 1) + 4 * (jj & 3); // feature of this lane's 8-byte word
+    for (int bb = 0; bb < BPW; ++bb) {
+      const int br = bg * BPW + bb;
 #pragma unroll
-      for (int r = 0; r < 2; ++r)
-        off_v[mt][r] = lds_chunk_offset<C::NCH>(tt + 8 * r, f >> 3) + (f & 7) * 2;
+      for (int k = 0; k < C::KL; ++k)
+        off_l[bb][k] = C::LAT_FLAT ? lat0 + (bb * (DB / 8) + 2 * k) * 16
+                                   : lds_chunk_offset<C::NCH>(n32, br * (DB / 8) + 2 * k + g);
+#pragma unroll
+      for (int mt = 0; mt < C::MT; ++mt) {
+        const int f = br * DB + 32 * mt + 16 * (q4 & 1) + 4 * (jj & 3); // feature of this lane's 8-byte word
+#pragma unroll
+        for (int r = 0; r < 2; ++r)
+          off_v[bb][mt][r] = C::LAT_FLAT ? val0 + (bb * (DB / 8) + 4 * mt) * 16 + r * (8 * C::NCH * 16 + 2 * 16)
+                                         : lds_chunk_offset<C::NCH>(tt + 8 * r, f >> 3) + (f & 7) * 2;
+      }
     }
   }
 
   // ---- running state ---------------------------------------------------------------------
-  f32x16 acc[C::HPW][C::MT];
-  float mref[C::HPW], lsum[C::HPW];
-  bool started[C::HPW];
+  f32x16 acc[C::HPW][BPW][C::MT];
+  float mref[C::HPW][BPW], lsum[C::HPW][BPW];
+  bool started[C::HPW][BPW];
   const float qs = p.q_scale;       // tau * log2(e) > 0
 #pragma unroll
-  for (int h = 0; h < C::HPW; ++h) {
+  for (int h = 0; h < C::HPW; ++h)
 #pragma unroll
-    for (int mt = 0; mt < C::MT; ++mt) acc[h][mt] = f32x16{};
-    mref[h] = -INFINITY;
-    lsum[h] = 0.f;
-    started[h] = false;
-  }
+    for (int bb = 0; bb < BPW; ++bb) {
+#pragma unroll
+      for (int mt = 0; mt < C::MT; ++mt) acc[h][bb][mt] = f32x16{};
+      mref[h][bb] = -INFINITY;
+      lsum[h][bb] = 0.f;
+      started[h][bb] = false;
+    }
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
   // ---- per-sub-tile building blocks ------------------------------------------------------
-  // scores of one 32-token sub-tile for every head group of this wave (raw units)
-  auto scores = [&](const lds_char* sub, f32x16 (&sc)[C::HPW]) __attribute__((always_inline)) {
-    bf16x8 ar[C::KR], al[C::KL];
+  // Scores of one 32-token sub-tile for every head group and branch of this wave (raw
+  // units). The RoPE part is the same for every branch: it is accumulated once into the
+  // first branch's tile, whose value then seeds (as the C operand) the latent chains of
+  // the other branches before the first branch continues its own.
+  auto scores = [&](const lds_char* sub, f32x16 (&sc)[C::HPW][BPW]) __attribute__((always_inline)) {
+    bf16x8 ar[C::KR], al[BPW][C::KL];
 #pragma unroll
     for (int k = 0; k < C::KR; ++k) ar[k] = *(const lds_bf16x8*)(sub + off_r[k]);
 #pragma unroll
-    for (int k = 0; k < C::KL; ++k) al[k] = *(const lds_bf16x8*)(sub + off_l[k]);
+    for (int bb = 0; bb < BPW; ++bb)
+#pragma unroll
+      for (int k = 0; k < C::KL; ++k) al[bb][k] = *(const lds_bf16x8*)(sub + off_l[bb][k]);
 #pragma unroll
     for (int h = 0; h < C::HPW; ++h) {
-      sc[h] = f32x16{};
+      sc[h][0] = f32x16{};
 #pragma unroll
-      for (int k = 0; k < C::KR; ++k) sc[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ar[k], qr[h][k], sc[h], 0, 0, 0);
+      for (int k = 0; k < C::KR; ++k)
+        sc[h][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ar[k], qr[h][k], sc[h][0], 0, 0, 0);
 #pragma unroll
-      for (int k = 0; k < C::KL; ++k) sc[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al[k], ql[h][k], sc[h], 0, 0, 0);
+      for (int bb = 1; bb < BPW; ++bb) {
+        sc[h][bb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al[bb][0], ql[h][bb][0], sc[h][0], 0, 0, 0);
+#pragma unroll
+        for (int k = 1; k < C::KL; ++k)
+          sc[h][bb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al[bb][k], ql[h][bb][k], sc[h][bb], 0, 0, 0);
+      }
+#pragma unroll
+      for (int k = 0; k < C::KL; ++k)
+        sc[h][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al[0][k], ql[h][0][k], sc[h][0], 0, 0, 0);
     }
   };
-  // transposed latent block [feature x token] of one sub-tile: two 4-token halves per K-chunk
-  auto values_a = [&](const lds_char* sub, bf16x8 (&av)[2][C::MT]) __attribute__((always_inline)) {
+  // transposed latent block [feature x token] of one sub-tile and branch: two 4-token
+  // halves per K-chunk
+  auto values_a = [&](const lds_char* sub, int bb, bf16x8 (&av)[2][C::MT]) __attribute__((always_inline)) {
 #pragma unroll
     for (int kc = 0; kc < 2; ++kc) {
 #pragma unroll
       for (int mt = 0; mt < C::MT; ++mt) {
-        const lds_char* a0 = sub + off_v[mt][0] + (16 * kc) * C::NCH * 16;
-        const lds_char* a1 = sub + off_v[mt][1] + (16 * kc) * C::NCH * 16;
+        const lds_char* a0 = sub + off_v[bb][mt][0] + (16 * kc) * C::NCH * 16;
+        const lds_char* a1 = sub + off_v[bb][mt][1] + (16 * kc) * C::NCH * 16;
         s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(a0));
         s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(a1));
         bf16x4 blo = __builtin_bit_cast(bf16x4, lo), bhi = __builtin_bit_cast(bf16x4, hi);
@@ -380,20 +438,20 @@ __global__ __launch_bounds__(W * 64, 1) void attn_mfma_kernel(AttnParams p) {
     }
   };
   // lazy running max: move the reference only when a logit exceeds it by more than the threshold
-  auto maybe_rescale = [&](int h, float mx) __attribute__((always_inline)) {
-    const float xm = fmaf(mx, qs, -mref[h]);
+  auto maybe_rescale = [&](int h, int bb, float mx) __attribute__((always_inline)) {
+    const float xm = fmaf(mx, qs, -mref[h][bb]);
     if (__builtin_amdgcn_ballot_w64(xm > kRescaleThreshold) != 0) {
-      const float d = fmaxf(fmaxf(xm, other_half(xm)), 0.f);
+      const float d = fmaxf(halves_max(xm), 0.f);
       const float f = __builtin_amdgcn_exp2f(-d);
-      mref[h] += d;
-      lsum[h] *= f;
+      mref[h][bb] += d;
+      lsum[h][bb] *= f;
 #pragma unroll
-      for (int mt = 0; mt < C::MT; ++mt) acc[h][mt] *= f;
+      for (int mt = 0; mt < C::MT; ++mt) acc[h][bb][mt] *= f;
     }
   };
   // p = 2^(x - m) packed to bf16; returns ls + the sum of the packed weights
-  auto weights = [&](int h, const f32x16& x, bf16x2 (&pk)[8], float ls) __attribute__((always_inline)) -> float {
-    const float negm = -mref[h];
+  auto weights = [&](int h, int bb, const f32x16& x, bf16x2 (&pk)[8], float ls) __attribute__((always_inline)) -> float {
+    const float negm = -mref[h][bb];
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
       f32x2 e = {__builtin_amdgcn_exp2f(fmaf(x[2 * k], qs, negm)), __builtin_amdgcn_exp2f(fmaf(x[2 * k + 1], qs, negm))};
@@ -402,8 +460,8 @@ __global__ __launch_bounds__(W * 64, 1) void attn_mfma_kernel(AttnParams p) {
     }
     return ls;
   };
-  // O += P.C for one sub-tile, reading the transposed latent one 32-feature tile at a time
-  auto pv_lds = [&](int h, const bf16x2 (&pk)[8], const lds_char* sub) __attribute__((always_inline)) {
+  // O += P.C for one sub-tile and branch, reading the transposed latent one 32-feature tile at a time
+  auto pv_lds = [&](int h, int bb, const bf16x2 (&pk)[8], const lds_char* sub) __attribute__((always_inline)) {
     bf16x8 pb[2];
 #pragma unroll
     for (int kc = 0; kc < 2; ++kc)
@@ -413,31 +471,31 @@ __global__ __launch_bounds__(W * 64, 1) void attn_mfma_kernel(AttnParams p) {
     for (int mt = 0; mt < C::MT; ++mt) {
 #pragma unroll
       for (int kc = 0; kc < 2; ++kc) {
-        const lds_char* a0 = sub + off_v[mt][0] + (16 * kc) * C::NCH * 16;
-        const lds_char* a1 = sub + off_v[mt][1] + (16 * kc) * C::NCH * 16;
+        const lds_char* a0 = sub + off_v[bb][mt][0] + (16 * kc) * C::NCH * 16;
+        const lds_char* a1 = sub + off_v[bb][mt][1] + (16 * kc) * C::NCH * 16;
         s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(a0));
         s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(a1));
         bf16x4 blo = __builtin_bit_cast(bf16x4, lo), bhi = __builtin_bit_cast(bf16x4, hi);
         const bf16x8 a = bf16x8{blo[0], blo[1], blo[2], blo[3], bhi[0], bhi[1], bhi[2], bhi[3]};
-        acc[h][mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kc], acc[h][mt], 0, 0, 0);
+        acc[h][bb][mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kc], acc[h][bb][mt], 0, 0, 0);
       }
     }
   };
-  // O += P.C for one sub-tile
-  auto pv = [&](int h, const bf16x2 (&pk)[8], const bf16x8 (&av)[2][C::MT]) __attribute__((always_inline)) {
+  // O += P.C for one sub-tile and branch
+  auto pv = [&](int h, int bb, const bf16x2 (&pk)[8], const bf16x8 (&av)[2][C::MT]) __attribute__((always_inline)) {
 #pragma unroll
     for (int kc = 0; kc < 2; ++kc) {
       bf16x8 pb = {pk[4 * kc][0], pk[4 * kc][1], pk[4 * kc + 1][0], pk[4 * kc + 1][1],
                    pk[4 * kc + 2][0], pk[4 * kc + 2][1], pk[4 * kc + 3][0], pk[4 * kc + 3][1]};
 #pragma unroll
       for (int mt = 0; mt < C::MT; ++mt)
-        acc[h][mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[kc][mt], pb, acc[h][mt], 0, 0, 0);
+        acc[h][bb][mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[kc][mt], pb, acc[h][bb][mt], 0, 0, 0);
     }
   };
-  auto accumulate = [&](int h, const f32x16& x, const bf16x8 (&av)[2][C::MT]) __attribute__((always_inline)) {
+  auto accumulate = [&](int h, int bb, const f32x16& x, const bf16x8 (&av)[2][C::MT]) __attribute__((always_inline)) {
     bf16x2 pk[8];
-    lsum[h] = weights(h, x, pk, lsum[h]);
-    pv(h, pk, av);
+    lsum[h][bb] = weights(h, bb, x, pk, lsum[h][bb]);
+    pv(h, bb, pk, av);
   };
 
   // ---- stages ------------------------------------------------------------------------------
@@ -452,41 +510,45 @@ __global__ __launch_bounds__(W * 64, 1) void attn_mfma_kernel(AttnParams p) {
       const int valid = t1 - (stage_tok0 + 32 * u);
       if (valid <= 0) continue;
       const lds_char* sub = stage + u * C::SUB_BYTES;
-      f32x16 sc[C::HPW];
+      f32x16 sc[C::HPW][BPW];
       scores(sub, sc);
-      bf16x8 av[2][C::MT];
-      values_a(sub, av);
 #pragma unroll
-      for (int h = 0; h < C::HPW; ++h) {
-        f32x16& x = sc[h];
-        if (valid < 32) {
+      for (int bb = 0; bb < BPW; ++bb) {
+        bf16x8 av[2][C::MT];
+        values_a(sub, bb, av);
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int tok = 8 * (r >> 2) + 4 * g + (r & 3);
-            if (tok >= valid) x[r] = -INFINITY;
+        for (int h = 0; h < C::HPW; ++h) {
+          f32x16& x = sc[h][bb];
+          if (valid < 32) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int tok = 8 * (r >> 2) + 4 * g + (r & 3);
+              if (tok >= valid) x[r] = -INFINITY;
+            }
           }
-        }
-        float mx = x[0];            // raw units (scale > 0 keeps the order)
+          float mx = x[0];            // raw units (scale > 0 keeps the order)
 #pragma unroll
-        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, x[r]);
-        if (!started[h]) {
-          mref[h] = fmaxf(mx, other_half(mx)) * qs;
-          started[h] = true;
-        } else {
-          maybe_rescale(h, mx);
+          for (int r = 1; r < 16; ++r) mx = fmaxf(mx, x[r]);
+          if (!started[h][bb]) {
+            mref[h][bb] = halves_max(mx) * qs;
+            started[h][bb] = true;
+          } else {
+            maybe_rescale(h, bb, mx);
+          }
+          accumulate(h, bb, x, av);
         }
-        accumulate(h, x, av);
       }
     }
   };
 
   // ---- main loop: full stages (the first seeds the running max), ragged last stage ----------
   const int nfull = (t1 - t0) / C::ST;       // stages with ST valid tokens
-  // Software pipeline over this wave's sub-tiles k = 0, 1, ... of the full stages: the
-  // score MFMAs of sub-tile k + 1 are issued before the softmax of sub-tile k, so the
-  // matrix cores work while the vector ALUs exponentiate. A ring slot is still read by
-  // the lagging P.C of its last sub-tile after the next stage's barrier, so the refill
-  // at stage s's barrier targets the slot of stage s - 2: LOOK = NS - 2 stages ahead.
+  // With one branch per wave the loop is software-pipelined over this wave's sub-tiles
+  // k = 0, 1, ... of the full stages: the score MFMAs of sub-tile k + 1 are issued before
+  // the softmax of sub-tile k, so the matrix cores work while the vector ALUs
+  // exponentiate. A ring slot is still read by the lagging P.C of its last sub-tile after
+  // the next stage's barrier, so the refill at stage s's barrier targets the slot of stage
+  // s - 2: LOOK = NS - 2 stages ahead (kept for the unpipelined loop too).
   constexpr int LOOK = C::NS - 2;
   for (int s = 0; s < LOOK && s < nst; ++s) issue_stage(s);
   auto begin_piped = [&](int s) __attribute__((always_inline)) {
@@ -500,42 +562,64 @@ __global__ __launch_bounds__(W * 64, 1) void attn_mfma_kernel(AttnParams p) {
     return stage_ptr(k / C::NSW) + ((k % C::NSW) * C::P + phase) * C::SUB_BYTES;
   };
   const int K = nfull * C::NSW;
-  // consume the scores `cur` of sub-tile k; first issue the scores of sub-tile k + 1 into `nxt`
-  auto step = [&](int k, f32x16 (&cur)[C::HPW], f32x16 (&nxt)[C::HPW]) __attribute__((always_inline)) {
-    if (k + 1 < K) {
-      if ((k + 1) % C::NSW == 0) begin_piped((k + 1) / C::NSW);
-      scores(sub_of(k + 1), nxt);
-    }
+  // softmax and P.C of sub-tile k from its scores
+  auto consume = [&](int k, f32x16 (&cur)[C::HPW][BPW]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int h = 0; h < C::HPW; ++h) {
-      bf16x2 pk[8];
-      float ls = weights(h, cur[h], pk, 0.f);
-      if (__builtin_amdgcn_ballot_w64(!(ls <= kStageSumMax)) != 0) {
-        float mx = cur[h][0];
+    for (int bb = 0; bb < BPW; ++bb)
 #pragma unroll
-        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, cur[h][r]);
-        maybe_rescale(h, mx);
-        ls = weights(h, cur[h], pk, 0.f);
+      for (int h = 0; h < C::HPW; ++h) {
+        bf16x2 pk[8];
+        float ls = weights(h, bb, cur[h][bb], pk, 0.f);
+        if (__builtin_amdgcn_ballot_w64(!(ls <= kStageSumMax)) != 0) {
+          float mx = cur[h][bb][0];
+#pragma unroll
+          for (int r = 1; r < 16; ++r) mx = fmaxf(mx, cur[h][bb][r]);
+          maybe_rescale(h, bb, mx);
+          ls = weights(h, bb, cur[h][bb], pk, 0.f);
+        }
+        lsum[h][bb] += ls;
+        pv_lds(h, bb, pk, sub_of(k));
       }
-      lsum[h] += ls;
-      pv_lds(h, pk, sub_of(k));
-    }
+  };
+  // the reference starts at the exact max of the first sub-tile
+  auto seed = [&](f32x16 (&sc)[C::HPW][BPW]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int h = 0; h < C::HPW; ++h)
+#pragma unroll
+      for (int bb = 0; bb < BPW; ++bb) {
+        float mx = sc[h][bb][0];
+#pragma unroll
+        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sc[h][bb][r]);
+        mref[h][bb] = halves_max(mx) * qs;
+        started[h][bb] = true;
+      }
   };
   if (K > 0) {
-    begin_piped(0);
-    f32x16 sa[C::HPW], sb[C::HPW];
-    scores(sub_of(0), sa);
-#pragma unroll
-    for (int h = 0; h < C::HPW; ++h) {   // the reference starts at the exact max of the first sub-tile
-      float mx = sa[h][0];
-#pragma unroll
-      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sa[h][r]);
-      mref[h] = fmaxf(mx, other_half(mx)) * qs;
-      started[h] = true;
-    }
-    for (int k = 0; k < K; k += 2) {
-      step(k, sa, sb);
-      if (k + 1 < K) step(k + 1, sb, sa);
+    if constexpr (C::PIPE) {
+      // consume the scores `cur` of sub-tile k; first issue the scores of sub-tile k + 1 into `nxt`
+      auto step = [&](int k, f32x16 (&cur)[C::HPW][BPW], f32x16 (&nxt)[C::HPW][BPW]) __attribute__((always_inline)) {
+        if (k + 1 < K) {
+          if ((k + 1) % C::NSW == 0) begin_piped((k + 1) / C::NSW);
+          scores(sub_of(k + 1), nxt);
+        }
+        consume(k, cur);
+      };
+      begin_piped(0);
+      f32x16 sa[C::HPW][BPW], sb[C::HPW][BPW];
+      scores(sub_of(0), sa);
+      seed(sa);
+      for (int k = 0; k < K; k += 2) {
+        step(k, sa, sb);
+        if (k + 1 < K) step(k + 1, sb, sa);
+      }
+    } else {
+      for (int k = 0; k < K; ++k) {
+        if (k % C::NSW == 0) begin_piped(k / C::NSW);
+        f32x16 sc[C::HPW][BPW];
+        scores(sub_of(k), sc);
+        if (k == 0) seed(sc);
+        consume(k, sc);
+      }
     }
   }
   if (nfull < nst) {
@@ -545,107 +629,126 @@ __global__ __launch_bounds__(W * 64, 1) void attn_mfma_kernel(AttnParams p) {
 
   // ---- combine halves, merge phases, write this split's partial state -----------------------
 #pragma unroll
-  for (int h = 0; h < C::HPW; ++h) lsum[h] += other_half(lsum[h]);
+  for (int h = 0; h < C::HPW; ++h)
+#pragma unroll
+    for (int bb = 0; bb < BPW; ++bb) lsum[h][bb] = halves_sum(lsum[h][bb]);
 
   if constexpr (C::P > 1) {
     block_barrier();   // every wave is done with the ring; reuse it for the merge records
     float* rec = reinterpret_cast<float*>(smem);
+    constexpr int RECF = (16 * C::MT + 2) * 64;     // floats of one (head group, branch) record
+    auto slot_of = [&](int q) __attribute__((always_inline)) {
+      return bg * (C::WPB - C::HGSPLIT) + (q - 1) * C::HGSPLIT + hgslot;
+    };
     if (phase > 0) {
-      const int slot = b * (C::WPB - C::HGSPLIT) + (phase - 1) * C::HGSPLIT + hgslot;
-      float* dst = rec + slot * C::MERGE_FLOATS;
+      float* dst = rec + slot_of(phase) * C::MERGE_FLOATS;
 #pragma unroll
-      for (int h = 0; h < C::HPW; ++h) {
-        float* d = dst + h * (16 * C::MT + 2) * 64;
+      for (int h = 0; h < C::HPW; ++h)
 #pragma unroll
-        for (int mt = 0; mt < C::MT; ++mt)
+        for (int bb = 0; bb < BPW; ++bb) {
+          float* d = dst + (h * BPW + bb) * RECF;
 #pragma unroll
-          for (int r = 0; r < 16; ++r) d[(16 * mt + r) * 64 + lane] = acc[h][mt][r];
-        d[(16 * C::MT) * 64 + lane] = mref[h];
-        d[(16 * C::MT + 1) * 64 + lane] = lsum[h];
-      }
+          for (int mt = 0; mt < C::MT; ++mt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) d[(16 * mt + r) * 64 + lane] = acc[h][bb][mt][r];
+          d[(16 * C::MT) * 64 + lane] = mref[h][bb];
+          d[(16 * C::MT + 1) * 64 + lane] = lsum[h][bb];
+        }
     }
     __syncthreads();
     if (phase > 0) return;
 #pragma unroll
-    for (int h = 0; h < C::HPW; ++h) {
-      float mstar = mref[h];
-      for (int q = 1; q < C::P; ++q) {
-        const float* d = rec + (b * (C::WPB - C::HGSPLIT) + (q - 1) * C::HGSPLIT + hgslot) * C::MERGE_FLOATS +
-                         h * (16 * C::MT + 2) * 64;
-        mstar = fmaxf(mstar, d[(16 * C::MT) * 64 + lane]);
+    for (int h = 0; h < C::HPW; ++h)
+#pragma unroll
+      for (int bb = 0; bb < BPW; ++bb) {
+        float mstar = mref[h][bb];
+        for (int q = 1; q < C::P; ++q) {
+          const float* d = rec + slot_of(q) * C::MERGE_FLOATS + (h * BPW + bb) * RECF;
+          mstar = fmaxf(mstar, d[(16 * C::MT) * 64 + lane]);
+        }
+        const float f0 = __builtin_amdgcn_exp2f(mref[h][bb] - mstar);
+        float l = lsum[h][bb] * f0;
+#pragma unroll
+        for (int mt = 0; mt < C::MT; ++mt) acc[h][bb][mt] *= f0;
+        for (int q = 1; q < C::P; ++q) {
+          const float* d = rec + slot_of(q) * C::MERGE_FLOATS + (h * BPW + bb) * RECF;
+          const float fq = __builtin_amdgcn_exp2f(d[(16 * C::MT) * 64 + lane] - mstar);
+          l += d[(16 * C::MT + 1) * 64 + lane] * fq;
+#pragma unroll
+          for (int mt = 0; mt < C::MT; ++mt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[h][bb][mt][r] += d[(16 * mt + r) * 64 + lane] * fq;
+        }
+        mref[h][bb] = mstar;
+        lsum[h][bb] = l;
       }
-      const float f0 = __builtin_amdgcn_exp2f(mref[h] - mstar);
-      float l = lsum[h] * f0;
-#pragma unroll
-      for (int mt = 0; mt < C::MT; ++mt) acc[h][mt] *= f0;
-      for (int q = 1; q < C::P; ++q) {
-        const float* d = rec + (b * (C::WPB - C::HGSPLIT) + (q - 1) * C::HGSPLIT + hgslot) * C::MERGE_FLOATS +
-                         h * (16 * C::MT + 2) * 64;
-        const float fq = __builtin_amdgcn_exp2f(d[(16 * C::MT) * 64 + lane] - mstar);
-        l += d[(16 * C::MT + 1) * 64 + lane] * fq;
-#pragma unroll
-        for (int mt = 0; mt < C::MT; ++mt)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) acc[h][mt][r] += d[(16 * mt + r) * 64 + lane] * fq;
-      }
-      mref[h] = mstar;
-      lsum[h] = l;
-    }
   }
 
 #pragma unroll
   for (int h = 0; h < C::HPW; ++h) {
     const int head = (hgslot * C::HPW + h) * 32 + n32;
     if (head >= p.H) continue;
-    const int64_t rec = (((int64_t)beta * p.num_splits + split) * p.H + head) * NB + b;
-    float* o = p.ws_o + rec * DB;
 #pragma unroll
-    for (int mt = 0; mt < C::MT; ++mt)
+    for (int bb = 0; bb < BPW; ++bb) {
+      const int64_t rec = (((int64_t)beta * p.num_splits + split) * p.H + head) * NB + bg * BPW + bb;
+      float* o = p.ws_o + rec * DB;
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        float4 v = make_float4(acc[h][mt][4 * q4], acc[h][mt][4 * q4 + 1], acc[h][mt][4 * q4 + 2], acc[h][mt][4 * q4 + 3]);
-        *reinterpret_cast<float4*>(o + 32 * mt + 8 * q4 + 4 * g) = v;
+      for (int mt = 0; mt < C::MT; ++mt)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          float4 v = make_float4(acc[h][bb][mt][4 * q4], acc[h][bb][mt][4 * q4 + 1], acc[h][bb][mt][4 * q4 + 2],
+                                 acc[h][bb][mt][4 * q4 + 3]);
+          *reinterpret_cast<float4*>(o + 32 * mt + 8 * q4 + 4 * g) = v;
+        }
+      if (g == 0) {
+        p.ws_ml[rec * 2] = mref[h][bb];
+        p.ws_ml[rec * 2 + 1] = lsum[h][bb];
       }
-    if (g == 0) {
-      p.ws_ml[rec * 2] = mref[h];
-      p.ws_ml[rec * 2 + 1] = lsum[h];
     }
   }
 }
 
-template <int NB, int DB, int DR, int HEADS, int W>
+template <int NB, int DB, int DR, int HEADS, int W, int BPW, int BPW_PAGED>
 hipError_t launch_shape(const AttnParams& p, bool paged, int grid_splits, hipStream_t stream) {
   dim3 grid(grid_splits, p.B);
   if (paged)
-    hipLaunchKernelGGL((attn_mfma_kernel<NB, DB, DR, HEADS, W, true>), grid, dim3(W * 64), 0, stream, p);
+    hipLaunchKernelGGL((attn_mfma_kernel<NB, DB, DR, HEADS, W, true, BPW_PAGED>), grid, dim3(W * 64), 0, stream, p);
   else
-    hipLaunchKernelGGL((attn_mfma_kernel<NB, DB, DR, HEADS, W, false>), grid, dim3(W * 64), 0, stream, p);
+    hipLaunchKernelGGL((attn_mfma_kernel<NB, DB, DR, HEADS, W, false, BPW>), grid, dim3(W * 64), 0, stream, p);
   return hipGetLastError();
 }
 
 }  // namespace
 
-// Shapes built with the MFMA path: (branches, branch width, RoPE width, heads, waves).
-#define MLRA_MFMA_SHAPES(X) \
-  X(4, 32, 32, 64, 16)      \
-  X(1, 128, 32, 64, 8)      \
-  X(1, 128, 32, 16, 4)      \
-  X(1, 32, 32, 16, 8)       \
-  X(1, 32, 32, 64, 8)       \
-  X(2, 64, 32, 64, 8)
+// Shapes built with the MFMA path: (branches, branch width, RoPE width, heads, waves,
+// branches per wave for a contiguous cache, for a paged cache). Two branches per wave share
+// the RoPE score. The paged MLRA-4 instance keeps one branch per wave: with two, its page
+// bookkeeping leaves the registers so short that the compiler adds copies to the loop and
+// it runs slower than with one. (Instances with different values sum the tokens of a split
+// in a different order, so paged and contiguous results then differ by rounding.)
+#ifndef MLRA4_BPW
+#define MLRA4_BPW 2
+#endif
+#define MLRA_MFMA_SHAPES(X)            \
+  X(4, 32, 32, 64, 16, MLRA4_BPW, 1)   \
+  X(1, 128, 32, 64, 8, 1, 1)           \
+  X(1, 128, 32, 16, 4, 1, 1)           \
+  X(1, 32, 32, 16, 8, 1, 1)            \
+  X(1, 32, 32, 64, 8, 1, 1)            \
+  X(2, 64, 32, 64, 8, 1, 1)
 
 int mfma_stage_tokens(int nb, int db, int dr, int heads) {
-#define X(xNB, xDB, xDR, xH, xW) \
-  if (nb == xNB && db == xDB && dr == xDR && heads == xH) return Cfg<xNB, xDB, xDR, xH, xW, false>::ST;
+#define X(xNB, xDB, xDR, xH, xW, xBPW, xBPWP) \
+  if (nb == xNB && db == xDB && dr == xDR && heads == xH) return Cfg<xNB, xDB, xDR, xH, xW, false, xBPW>::ST;
   MLRA_MFMA_SHAPES(X)
 #undef X
   return 0;
 }
 
 hipError_t launch_attn_mfma(const AttnParams& p, bool paged, int grid_splits, hipStream_t stream) {
-#define X(xNB, xDB, xDR, xH, xW) \
+#define X(xNB, xDB, xDR, xH, xW, xBPW, xBPWP) \
   if (p.NB == xNB && p.DB == xDB && p.DR == xDR && p.H == xH) \
-    return launch_shape<xNB, xDB, xDR, xH, xW>(p, paged, grid_splits, stream);
+    return launch_shape<xNB, xDB, xDR, xH, xW, xBPW, xBPWP>(p, paged, grid_splits, stream);
   MLRA_MFMA_SHAPES(X)
 #undef X
   return hipErrorInvalidValue;

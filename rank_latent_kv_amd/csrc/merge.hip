@@ -146,7 +146,6 @@ __global__ __launch_bounds__(kMergeThreads) void merge_mfma_kernel(MergeParams p
   constexpr int PAR = kMergeThreads / ITEMS >= 1 ? kMergeThreads / ITEMS : 1;   // threads per item
   constexpr int UROW = DC + 8;
   static_assert(ITEMS * PAR <= kMergeThreads || PAR == 1, "item mapping");
-  __shared__ int nsplit[SEQB];
   __shared__ float red_m[PAR][ITEMS], red_l[PAR][ITEMS];
   __shared__ float4 red_o[PAR][ITEMS];
   __shared__ __attribute__((aligned(16))) __bf16 uhi[16][UROW];
@@ -158,7 +157,39 @@ __global__ __launch_bounds__(kMergeThreads) void merge_mfma_kernel(MergeParams p
   const int NB = p.NB, DB = p.DB, S = p.num_splits;
   const int r16 = lane & 15, kg = lane >> 4;
 
-  // W^V_i operands of this wave's tiles (prefetched; used at the end)
+  // this thread's (sequence, 4 features) item and its slice of the splits
+  const int item = tid % ITEMS, part = tid / ITEMS;
+  const int bl = item / (DC / 4);
+  const int k = (item % (DC / 4)) * 4;
+  const int b = k / DB;
+  const int beta = beta0 + bl;
+  const bool active = part < PAR && beta < p.B;
+  const int beta_c = beta < p.B ? beta : p.B - 1;
+
+  // loads of one round of kChunk splits (clamped to the last split; unused ones are discarded)
+  float mv[kChunk], lv[kChunk];
+  float4 ov[kChunk];
+  auto load_round = [&](int s0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < kChunk; ++j) {
+      const int sp = s0 + j * PAR;
+      const int spc = sp < S ? sp : S - 1;
+      const int64_t rec = (((int64_t)beta_c * S + spc) * p.H + head) * NB + b;
+      const float2 ml = *reinterpret_cast<const float2*>(p.ws_ml + rec * 2);
+      mv[j] = ml.x;
+      lv[j] = ml.y;
+      ov[j] = *reinterpret_cast<const float4*>(p.ws_o + rec * DB + (k - b * DB));
+    }
+  };
+  // Order of the requests: the sequence length and the first round of partials, then the
+  // W^V_i operands (needed last), so that one memory latency covers them all.
+  int ns = 0;
+  if (active) {
+    int L = p.seq_lens[beta];
+    L = L < 0 ? 0 : (L > p.max_seq_len ? p.max_seq_len : L);
+    ns = (L + p.split_tokens - 1) / p.split_tokens;
+    load_round(part);
+  }
   const __bf16* wv = reinterpret_cast<const __bf16*>(p.w_v) + (int64_t)head * DH * DC;
   bf16x8 wreg[NTW][KC];
 #pragma unroll
@@ -170,45 +201,18 @@ __global__ __launch_bounds__(kMergeThreads) void merge_mfma_kernel(MergeParams p
                                   wv + (int64_t)(nt * 16 + r16) * DC + 32 * kc + 8 * kg))
                             : bf16x8{};
   }
-  if (tid < SEQB) {
-    const int beta = beta0 + tid;
-    int ns = 0;
-    if (beta < p.B) {
-      int L = p.seq_lens[beta];
-      L = L < 0 ? 0 : (L > p.max_seq_len ? p.max_seq_len : L);
-      ns = (L + p.split_tokens - 1) / p.split_tokens;
-    }
-    nsplit[tid] = ns;
-  }
   for (int i = tid; i < 16 * UROW; i += kMergeThreads) {
     (&uhi[0][0])[i] = (__bf16)0.f;
     (&ulo[0][0])[i] = (__bf16)0.f;
   }
-  __syncthreads();
 
   // 1. partial merges over this thread's splits
-  const int item = tid % ITEMS, part = tid / ITEMS;
-  const int bl = item / (DC / 4);
-  const int k = (item % (DC / 4)) * 4;
-  const int b = k / DB;
-  const int beta = beta0 + bl;
   if (part < PAR) {
-    const int ns = nsplit[bl];
     float m_loc = -INFINITY, l_loc = 0.f;
     float4 o_loc = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (beta < p.B) {
+    if (active) {
       for (int s0 = part; s0 < S; s0 += PAR * kChunk) {
-        float mv[kChunk], lv[kChunk];
-        float4 ov[kChunk];
-#pragma unroll
-        for (int j = 0; j < kChunk; ++j) {
-          const int sp = s0 + j * PAR;
-          const int spc = sp < S ? sp : S - 1;
-          const int64_t rec = (((int64_t)beta * S + spc) * p.H + head) * NB + b;
-          mv[j] = p.ws_ml[rec * 2];
-          lv[j] = p.ws_ml[rec * 2 + 1];
-          ov[j] = *reinterpret_cast<const float4*>(p.ws_o + rec * DB + (k - b * DB));
-        }
+        if (s0 != part) load_round(s0);
         float mc = m_loc;
 #pragma unroll
         for (int j = 0; j < kChunk; ++j) {
