@@ -190,6 +190,33 @@ def reduce_pmc(workload: str, fetch_csv: str, write_csv: str, command: str) -> s
     return "\n".join(lines) + "\n"
 
 
+def read_probe(sizes=(167_772_160, 536_870_912), calls=50):
+    """The box's practical streaming-read rate: the library's read probe (one coalesced
+    stream of 16-byte nontemporal loads) over buffers of the headline and TP-shard cache
+    sizes, rotating enough copies (>= 512 MiB) that the Infinity Cache cannot serve them,
+    timed with events around all calls."""
+    dev = torch.device("cuda:0")
+    res = []
+    for nbytes in sizes:
+        copies = max(1, math.ceil(ROTATE_BYTES / nbytes))
+        bufs = [torch.ones(nbytes // 4, dtype=torch.int32, device=dev) for _ in range(copies)]
+        out = torch.empty(int(R.lib().mlra_read_probe_words()), dtype=torch.int32, device=dev)
+        for k in range(5):
+            R.read_probe(bufs[k % copies], out)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for k in range(calls):
+            R.read_probe(bufs[k % copies], out)
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / calls
+        res.append({"bytes": nbytes, "us_per_read": us, "tbps": nbytes / us / 1e6, "copies": copies})
+        del bufs
+        torch.cuda.empty_cache()
+    return {"read_probe": res, "peak_tbps": HBM_PEAK_GBPS / 1e3, "op": "mlra_read_probe"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -210,6 +237,9 @@ def main():
     ap.add_argument("--pmc-reduce", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="no GPU run: reduce two rocprofv3 counter files of --workload into profiles/")
     ap.add_argument("--pmc-command", default="", help="with --pmc-reduce: the command that made the files")
+    ap.add_argument("--read-probe", action="store_true",
+                    help="only measure this GPU's streaming-read rate (the library's read probe over rotated "
+                         "buffers of the headline and TP-shard cache sizes) and print it as one JSON line")
     args = ap.parse_args()
 
     if args.pmc_reduce:
@@ -224,6 +254,9 @@ def main():
         print(json.dumps({"error": "this build runs on one GPU only: the decode kernel is measured on one "
                                    "GPU's share; multi-GPU sharding is a design note, not implemented"}))
         sys.exit(2)
+    if args.read_probe:
+        print(json.dumps(read_probe()))
+        return
 
     w = PRESETS[args.workload]
     if args.batch:

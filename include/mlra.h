@@ -295,6 +295,21 @@ mlra_status mlra_page_pool_free(mlra_page_pool* pool, int32_t n, const int32_t* 
 int32_t mlra_page_pool_num_free(const mlra_page_pool* pool);
 void mlra_page_pool_destroy(mlra_page_pool* pool);
 
+/*
+ * Measurement support: a streaming-read probe. Reads the `bytes` bytes at device
+ * pointer `src` once, as one coalesced stream of 16-byte nontemporal loads, so that a
+ * caller can time the read rate this GPU reaches (the practical ceiling next to the
+ * HBM peak against which the attention kernel's bandwidth is judged). Writes
+ * mlra_read_probe_words() 32-bit words to device buffer `out`: out[g] is the XOR of
+ * the 32-bit words read by work-group g, so the XOR of all of them equals the XOR of
+ * every 32-bit word of the buffer. Enqueued on `stream` without waiting.
+ * Errors (no HIP call made): MLRA_ERR_INVALID_ARG if a pointer is NULL, `bytes` is 0
+ * or not a multiple of 16, `src` is not 16-byte aligned, or `out_words` is smaller
+ * than mlra_read_probe_words(); MLRA_ERR_HIP if the launch fails.
+ */
+int32_t mlra_read_probe_words(void);
+mlra_status mlra_read_probe(const void* src, size_t bytes, uint32_t* out, int32_t out_words, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

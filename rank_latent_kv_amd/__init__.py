@@ -32,7 +32,7 @@ EXPORTED_SYMBOLS = (
     "mlra_last_error", "mlra_version", "mlra_decode_workspace_size", "mlra_decode_validate", "mlra_decode",
     "mla_decode", "mlra_paged_append", "mlra_paged_gather", "mlra_page_table_check", "mlra_page_pool_create",
     "mlra_page_pool_alloc", "mlra_page_pool_free", "mlra_page_pool_num_free", "mlra_page_pool_destroy",
-    "mlra_decode_prepare",
+    "mlra_decode_prepare", "mlra_read_probe_words", "mlra_read_probe",
 )
 
 
@@ -108,9 +108,12 @@ def lib() -> ctypes.CDLL:
         L.mlra_page_pool_num_free.restype = i32
         L.mlra_page_pool_destroy.argtypes = [vp]
         L.mlra_page_pool_destroy.restype = None
+        L.mlra_read_probe_words.argtypes = []
+        L.mlra_read_probe_words.restype = i32
+        L.mlra_read_probe.argtypes = [vp, ctypes.c_size_t, vp, i32, vp]
         for name in ("mlra_decode_validate", "mlra_decode", "mla_decode", "mlra_decode_prepare", "mlra_paged_append",
                      "mlra_paged_gather", "mlra_page_table_check", "mlra_page_pool_create",
-                     "mlra_page_pool_alloc", "mlra_page_pool_free"):
+                     "mlra_page_pool_alloc", "mlra_page_pool_free", "mlra_read_probe"):
             getattr(L, name).restype = i32
         _lib = L
     return _lib
@@ -349,3 +352,15 @@ class PagePool:
             self.close()
         except Exception:
             pass
+
+
+def read_probe(buf: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Read every byte of the device tensor `buf` once (streaming-read probe) and return the
+    per-work-group XOR words (int32 [mlra_read_probe_words()]) on the current stream."""
+    n = int(lib().mlra_read_probe_words())
+    if out is None:
+        out = torch.empty(n, dtype=torch.int32, device=buf.device)
+    _check(lib().mlra_read_probe(ctypes.c_void_p(buf.data_ptr()), buf.numel() * buf.element_size(),
+                                 ctypes.c_void_p(out.data_ptr()), out.numel(),
+                                 ctypes.c_void_p(torch.cuda.current_stream(buf.device).cuda_stream)))
+    return out

@@ -22,7 +22,7 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmlra.so")
 ARCH = "gfx950"
 
-SOURCES = ["attn_mfma.hip", "attn_generic.hip", "merge.hip", "paged.hip", "prepare.hip", "mlra_api.cpp"]
+SOURCES = ["attn_mfma.hip", "attn_generic.hip", "merge.hip", "paged.hip", "prepare.hip", "read_probe.hip", "mlra_api.cpp"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC,
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-Wno-unused-result", "-Wno-inline-asm"]

@@ -370,6 +370,19 @@ mlra_status mlra_decode_prepare(const mlra_prepare_args* a, void* stream) {
   return ok();
 }
 
+int32_t mlra_read_probe_words(void) { return mlra::kProbeBlocks; }
+
+mlra_status mlra_read_probe(const void* src, size_t bytes, uint32_t* out, int32_t out_words, void* stream) {
+  if (!src || !out) return fail(MLRA_ERR_INVALID_ARG, "a required pointer is NULL");
+  if (bytes == 0 || bytes % 16 != 0) return fail(MLRA_ERR_INVALID_ARG, "bytes must be a positive multiple of 16 (got %zu)", bytes);
+  if (!aligned(src, 16)) return fail(MLRA_ERR_INVALID_ARG, "src must be 16-byte aligned");
+  if (out_words < mlra::kProbeBlocks)
+    return fail(MLRA_ERR_INVALID_ARG, "out holds %d words, needs %d", out_words, mlra::kProbeBlocks);
+  hipError_t e = mlra::launch_read_probe(src, (int64_t)bytes, out, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "read probe launch");
+  return ok();
+}
+
 mlra_status mlra_paged_append(void* pool, int64_t row_stride, int32_t row_elems, int32_t page_size, int32_t num_pages,
                               const int32_t* page_table, int32_t max_pages, const int32_t* positions, const void* rows,
                               int32_t batch, int32_t dtype, uint32_t* error_flags, void* stream) {

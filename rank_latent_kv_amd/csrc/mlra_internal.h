@@ -74,6 +74,12 @@ size_t merge_lds_bytes(int nb, int db, int num_splits);
 constexpr size_t kMergeLdsLimit = 60 * 1024;
 hipError_t launch_merge(const MergeParams& p, hipStream_t stream);
 
+// Streaming-read probe (measurement support): kProbeBlocks work-groups of kProbeThreads
+// threads; out[g] = XOR of the 32-bit words work-group g read.
+constexpr int kProbeBlocks = 4096;
+constexpr int kProbeThreads = 256;
+hipError_t launch_read_probe(const void* src, int64_t bytes, uint32_t* out, hipStream_t stream);
+
 // The step before a decode call: query absorption, RoPE rotation, new cache rows.
 struct PrepareParams {
   int B, H, NB, DB, DR, DH;

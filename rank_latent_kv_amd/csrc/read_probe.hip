@@ -1,0 +1,52 @@
+// Streaming-read probe: the HBM read rate this GPU actually reaches with a plain
+// coalesced stream, the practical ceiling next to the 8 TB/s peak for judging the
+// attention kernel's bandwidth. Every 16-byte word of the buffer is read once with a
+// nontemporal load; each work-group writes the XOR of the 32-bit words it read, so the
+// loads cannot be dropped and the host can check the result bit for bit.
+#include <hip/hip_runtime.h>
+
+#include "mlra_internal.h"
+
+namespace mlra {
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__global__ __launch_bounds__(kProbeThreads) void read_probe_kernel(const u32x4* __restrict__ src, int64_t n16,
+                                                                    uint32_t* __restrict__ out) {
+  const int64_t stride = (int64_t)gridDim.x * kProbeThreads;
+  int64_t i = (int64_t)blockIdx.x * kProbeThreads + threadIdx.x;
+  uint32_t acc = 0;
+  // four independent loads in flight per thread per trip
+  for (; i + 3 * stride < n16; i += 4 * stride) {
+    const u32x4 a = __builtin_nontemporal_load(src + i);
+    const u32x4 b = __builtin_nontemporal_load(src + i + stride);
+    const u32x4 c = __builtin_nontemporal_load(src + i + 2 * stride);
+    const u32x4 d = __builtin_nontemporal_load(src + i + 3 * stride);
+    const u32x4 x = a ^ b ^ c ^ d;
+    acc ^= x.x ^ x.y ^ x.z ^ x.w;
+  }
+  for (; i < n16; i += stride) {
+    const u32x4 a = __builtin_nontemporal_load(src + i);
+    acc ^= a.x ^ a.y ^ a.z ^ a.w;
+  }
+  for (int off = 32; off > 0; off >>= 1) acc ^= __shfl_xor(acc, off, 64);
+  __shared__ uint32_t part[kProbeThreads / 64];
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t r = 0;
+    for (int w = 0; w < kProbeThreads / 64; ++w) r ^= part[w];
+    out[blockIdx.x] = r;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_read_probe(const void* src, int64_t bytes, uint32_t* out, hipStream_t stream) {
+  hipLaunchKernelGGL(read_probe_kernel, dim3(kProbeBlocks), dim3(kProbeThreads), 0, stream,
+                     static_cast<const u32x4*>(src), bytes / 16, out);
+  return hipGetLastError();
+}
+
+}  // namespace mlra

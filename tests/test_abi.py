@@ -378,3 +378,21 @@ def test_prepare_rejects_positions_outside_the_cache():
     a = prepare_args(positions_host=ctypes.cast(pos, ctypes.c_void_p).value)
     assert R.lib().mlra_decode_prepare(ctypes.byref(a), None) == R.MLRA_ERR_INVALID_ARG
     assert "outside the cache" in R.last_error()
+
+
+@pytest.mark.parametrize("src,nbytes,out,words,msg", [
+    (0, 4096, 256, 4096, "NULL"),
+    (256, 4096, 0, 4096, "NULL"),
+    (256, 0, 256, 4096, "multiple of 16"),
+    (256, 4100, 256, 4096, "multiple of 16"),
+    (264, 4096, 256, 4096, "aligned"),
+    (256, 4096, 256, 7, "needs"),
+])
+def test_read_probe_validation(src, nbytes, out, words, msg):
+    """Argument errors of the streaming-read probe come back before any HIP call (the
+    pointers here are never dereferenced)."""
+    L = R.lib()
+    assert L.mlra_read_probe_words() >= 1
+    st = L.mlra_read_probe(ctypes.c_void_p(src), nbytes, ctypes.c_void_p(out), words, None)
+    assert st == R.MLRA_ERR_INVALID_ARG
+    assert msg in R.last_error()
