@@ -156,7 +156,9 @@ def make_args(q_lat, q_rope, kv_lat, kv_rope, seq_lens, w_v, *, sm_scale: float,
     """Fill ``mlra_decode_args`` from tensors (shapes as in include/mlra.h).
 
     ``kv_lat`` / ``kv_rope`` may be views into one combined [.., rows, d_c + d_R]
-    tensor; ``row_stride`` / ``seq_stride`` default to that tensor's strides."""
+    tensor; ``row_stride`` / ``seq_stride`` default to that tensor's strides. The struct
+    holds raw pointers, so it keeps a reference to every tensor it points into: the
+    memory stays valid for as long as the struct is alive."""
     B, H, NB, DB = q_lat.shape
     DR = q_rope.shape[-1]
     a = DecodeArgs()
@@ -189,6 +191,7 @@ def make_args(q_lat, q_rope, kv_lat, kv_rope, seq_lens, w_v, *, sm_scale: float,
     a.error_flags = _ptr(error_flags)
     if events is not None:
         a.event_attn_begin, a.event_attn_end = events
+    a._keep = (q_lat, q_rope, kv_lat, kv_rope, seq_lens, seq_lens_host, page_table, w_v, out, workspace, error_flags)
     return a
 
 
@@ -220,6 +223,11 @@ def _run(fn_name: str, q_lat, q_rope, kv_lat, kv_rope, seq_lens, w_v, *, sm_scal
         workspace = alloc_workspace(args, q_lat.device)
         args.workspace = workspace.data_ptr()
         args.workspace_bytes = workspace.numel()
+        args._keep = args._keep + (workspace,)
+        if stream is not None and isinstance(stream, torch.cuda.Stream):
+            # the workspace comes from the current stream's pool but is used on `stream`:
+            # keep the allocator from handing it out again before that stream's work ends
+            workspace.record_stream(stream)
     _check(getattr(lib(), fn_name)(ctypes.byref(args), _stream_handle(stream)))
     return out
 
@@ -243,7 +251,8 @@ def make_prepare_args(q_nope, q_pe, w_uk_t, c_new, k_pe_new, positions, kv_lat, 
                       seq_stride: Optional[int] = None, max_seq_len: Optional[int] = None,
                       page_table: Optional[torch.Tensor] = None, page_size: int = 64, num_pages: int = 0,
                       error_flags: Optional[torch.Tensor] = None) -> PrepareArgs:
-    """Fill ``mlra_prepare_args`` (shapes as in include/mlra.h; w_uk_t is [h, d_c, d_h])."""
+    """Fill ``mlra_prepare_args`` (shapes as in include/mlra.h; w_uk_t is [h, d_c, d_h]). The struct
+    keeps a reference to every tensor it points into."""
     B, H, DH = q_nope.shape
     DC = w_uk_t.shape[1]
     a = PrepareArgs()
@@ -265,6 +274,9 @@ def make_prepare_args(q_nope, q_pe, w_uk_t, c_new, k_pe_new, positions, kv_lat, 
     else:
         a.page_table, a.max_pages, a.page_size, a.num_pages = _ptr(page_table), page_table.shape[1], page_size, num_pages
     a.error_flags = _ptr(error_flags)
+    # the struct holds raw pointers: keep the tensors behind them alive with it
+    a._keep = (q_nope, q_pe, w_uk_t, c_new, k_pe_new, positions, positions_host, kv_lat, kv_rope, q_lat, q_rope,
+               page_table, error_flags)
     return a
 
 

@@ -396,3 +396,31 @@ def test_read_probe_validation(src, nbytes, out, words, msg):
     st = L.mlra_read_probe(ctypes.c_void_p(src), nbytes, ctypes.c_void_p(out), words, None)
     assert st == R.MLRA_ERR_INVALID_ARG
     assert msg in R.last_error()
+
+
+def test_arg_structs_keep_their_tensors_alive():
+    """The ctypes structs hold raw pointers; they must keep the tensors behind them alive, or
+    a caller that drops its own references leaves them pointing at freed memory."""
+    import gc
+    import weakref
+    B, H, NB, DB, DR, DH, L = 2, 4, 4, 8, 8, 16, 8
+    ws = torch.empty(64, dtype=torch.uint8)
+    ref = weakref.ref(ws)
+    a = R.make_args(torch.zeros(B, H, NB, DB), torch.zeros(B, H, DR), torch.zeros(B, L, NB * DB + DR)[..., :NB * DB],
+                    torch.zeros(B, L, NB * DB + DR)[..., NB * DB:], torch.zeros(B, dtype=torch.int32),
+                    torch.zeros(H, DH, NB * DB), sm_scale=1.0, alpha=1.0, workspace=ws)
+    del ws
+    gc.collect()
+    assert ref() is not None and ref().data_ptr() == a.workspace
+    qn = torch.zeros(B, H, DH)
+    qref = weakref.ref(qn)
+    pa = R.make_prepare_args(qn, torch.zeros(B, H, DR), torch.zeros(H, NB * DB, DH), torch.zeros(B, NB * DB),
+                             torch.zeros(B, DR), torch.zeros(B, dtype=torch.int32), torch.zeros(B, L, NB * DB),
+                             torch.zeros(B, L, DR), num_branches=NB, q_lat=torch.zeros(B, H, NB, DB),
+                             q_rope=torch.zeros(B, H, DR))
+    del qn
+    gc.collect()
+    assert qref() is not None and qref().data_ptr() == pa.q_nope
+    del a, pa
+    gc.collect()
+    assert ref() is None and qref() is None
