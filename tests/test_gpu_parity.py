@@ -192,3 +192,34 @@ def test_caller_workspace_reuse():
     y2 = gpu_decode(w, inp, workspace=ws)
     assert torch.equal(y1, y2)
     assert row_rel_err(f64(y1), oracle_decode(w, inp)) <= TOL_BF16
+
+
+@pytest.mark.parametrize("fill", [float("nan"), float("inf"), float("-inf"), 1e30])
+@pytest.mark.parametrize("preset,mla", [("mlra4_b16_l32k", False), ("mla_b16_l32k", True),
+                                        ("mlra4_paged_b4_l64k_128k", False)])
+def test_unwritten_split_records_are_ignored(fill, preset, mla):
+    """With ragged lengths the shorter sequences leave split records of the workspace
+    unwritten; whatever the caller's workspace held there (NaN, infinities, huge values)
+    must not reach the output."""
+    lens = [9000, 300, 5000, 2100]
+    w = PRESETS[preset].replace(batch=len(lens))
+    inp = make_inputs(w, seq_lens=lens)
+    d = {k: v.to(DEV) for k, v in inp.items()}
+    dc = w.latent_dim
+    if w.paged:
+        pool = d["pool"]
+        args = R.make_args(d["q_lat"], d["q_rope"], pool[..., :dc], pool[..., dc:], d["seq_lens"], d["w_v"],
+                           sm_scale=w.sm_scale, alpha=w.alpha, page_table=d["page_table"], page_size=w.page_size,
+                           num_pages=pool.shape[0], row_stride=pool.shape[-1], max_seq_len=max(lens),
+                           seq_lens_host=inp["seq_lens"].to(torch.int32), num_splits=12)
+    else:
+        q_lat = d["q_lat"]
+        args = R.make_args(q_lat, d["q_rope"], d["kv"][..., :dc], d["kv"][..., dc:], d["seq_lens"], d["w_v"],
+                           sm_scale=w.sm_scale, alpha=w.alpha, seq_lens_host=inp["seq_lens"].to(torch.int32),
+                           num_splits=12)
+    n = R.workspace_size(args)
+    ws = torch.full((n // 4,), fill, dtype=torch.float32, device=DEV)
+    say(f"unwritten records filled with {fill}, {preset}")
+    y = f64(gpu_decode(w, inp, mla=mla, num_splits=12, workspace=ws))
+    assert np.all(np.isfinite(y))
+    assert row_rel_err(y, oracle_decode(w, inp)) <= TOL_BF16
