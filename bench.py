@@ -387,7 +387,8 @@ def main():
                      "frac": achieved_gbps / HBM_PEAK_GBPS,
                      "traffic": traffic,
                      "kernel": "attn_mfma_kernel", "algorithmic_bytes_per_launch": ab["attention_kernel"],
-                     "avg_launch_us": attn_s * 1e6, "p10_us": float(np.percentile(attn_ms, 10)) * 1e3,
+                     "avg_launch_us": attn_s * 1e6, "median_us": float(np.median(attn_ms)) * 1e3,
+                     "p10_us": float(np.percentile(attn_ms, 10)) * 1e3,
                      "p90_us": float(np.percentile(attn_ms, 90)) * 1e3,
                      "event_samples": len(evs), "event_every": every,
                      "mfma_tflops": af["attention"] / attn_s / 1e12},
