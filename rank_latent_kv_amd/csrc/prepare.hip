@@ -9,9 +9,12 @@
 // m * base^(-2j/d_R). The angle and its sine and cosine are computed in fp64 so
 // that long positions keep their accuracy; the rotation itself runs in fp32.
 //
-// One work-group per head does the absorption of that head for every sequence; one
-// work-group per sequence computes the sequence's rotation angles once (fp64, into
-// LDS), rotates the RoPE query of every head and writes the cache row. For
+// On the MFMA path each wave of the absorption work-groups computes one 16-column tile of
+// one head's absorbed queries for every sequence (a head's tiles spread over
+// ceil(d_c / 64) groups), issuing all of its loads before its first MFMA; one work-group
+// per sequence computes the sequence's rotation angles once (fp64, into LDS), rotates the
+// RoPE query of every head and writes the cache row, with its first query loads issued
+// before the angles are computed. For
 // bf16 with d_h % 32 == 0 (at most 256) and d_c % 16 == 0 the absorption runs on
 // 16x16x32 MFMAs, each wave loading all its operands before its first MFMA:
 //   Q~[seq x d_c] = Q^N[seq x d_h] . W^UK_i[d_h x d_c],
@@ -53,45 +56,52 @@ __device__ __forceinline__ void rope_cs(int m, int j, int dr, double base, float
   *s = (float)sd;
 }
 
+// Absorption work-groups per head: on the MFMA path one 16-column output tile per wave, so
+// that every wave issues all of its loads at once; otherwise one group per head.
+__host__ __device__ inline int absorb_groups(const PrepareParams& p) {
+  constexpr int kWaves = kPrepThreads / 64;
+  return p.mfma ? (p.NB * p.DB / 16 + kWaves - 1) / kWaves : 1;
+}
+
+constexpr int kQPre = 4;   // RoPE-query pairs per thread loaded before the angles are known
+
 __global__ __launch_bounds__(kPrepThreads) void prepare_kernel(PrepareParams p) {
   const int tid = threadIdx.x;
   const int DC = p.NB * p.DB;
-  if (blockIdx.x < (unsigned)p.H) {
-    const int head = blockIdx.x;
+  const int ag = absorb_groups(p);
+  if (blockIdx.x < (unsigned)(p.H * ag)) {
+    const int head = blockIdx.x / ag;
     // ---- absorption ----------------------------------------------------------------------
     if (p.mfma) {
       const int lane = tid & 63, wave = tid >> 6;
       const int r16 = lane & 15, kg = lane >> 4;
+      const int nt = (blockIdx.x - head * ag) * (kPrepThreads / 64) + wave;   // this wave's output tile
+      if (nt >= DC / 16) return;
+      const int kchunks = p.DH / 32;
       const __bf16* qn = reinterpret_cast<const __bf16*>(p.q_nope);
-      const __bf16* w = reinterpret_cast<const __bf16*>(p.w_uk) + (int64_t)head * DC * p.DH;
-      const int ntiles = DC / 16, kchunks = p.DH / 32;
+      const __bf16* wrow = reinterpret_cast<const __bf16*>(p.w_uk) + ((int64_t)head * DC + 16 * nt + r16) * p.DH;
+      // B operands (W^UK_i rows of this tile), used for every block of 16 sequences
+      bf16x8 b[kMaxKc];
+#pragma unroll
+      for (int kc = 0; kc < kMaxKc; ++kc)
+        if (kc < kchunks) b[kc] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(wrow + 32 * kc + 8 * kg));
       for (int m0 = 0; m0 < p.B; m0 += 16) {
         const int beta_a = m0 + r16;                 // A row of this lane
-        // A operands of every K-chunk (chunks past d_h repeat the last one and are not used)
         bf16x8 a[kMaxKc];
 #pragma unroll
-        for (int kc = 0; kc < kMaxKc; ++kc) {
-          const int k0 = 32 * min(kc, kchunks - 1) + 8 * kg;
-          a[kc] = beta_a < p.B ? __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(
-                                     qn + ((int64_t)beta_a * p.H + head) * p.DH + k0))
-                               : bf16x8{};
-        }
-        for (int nt = wave; nt < ntiles; nt += kPrepThreads / 64) {
-          bf16x8 b[kMaxKc];
+        for (int kc = 0; kc < kMaxKc; ++kc)
+          if (kc < kchunks)
+            a[kc] = beta_a < p.B ? __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(
+                                       qn + ((int64_t)beta_a * p.H + head) * p.DH + 32 * kc + 8 * kg))
+                                 : bf16x8{};
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int kc = 0; kc < kMaxKc; ++kc) {
-            const int k0 = 32 * min(kc, kchunks - 1) + 8 * kg;
-            b[kc] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(w + (int64_t)(16 * nt + r16) * p.DH + k0));
-          }
-          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        for (int kc = 0; kc < kMaxKc; ++kc)
+          if (kc < kchunks) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[kc], b[kc], acc, 0, 0, 0);
 #pragma unroll
-          for (int kc = 0; kc < kMaxKc; ++kc)
-            if (kc < kchunks) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[kc], b[kc], acc, 0, 0, 0);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int beta = m0 + 4 * kg + r;
-            if (beta < p.B) st(p.q_lat, ((int64_t)beta * p.H + head) * DC + 16 * nt + r16, acc[r], p.dtype);
-          }
+        for (int r = 0; r < 4; ++r) {
+          const int beta = m0 + 4 * kg + r;
+          if (beta < p.B) st(p.q_lat, ((int64_t)beta * p.H + head) * DC + 16 * nt + r16, acc[r], p.dtype);
         }
       }
     } else {
@@ -106,20 +116,39 @@ __global__ __launch_bounds__(kPrepThreads) void prepare_kernel(PrepareParams p) 
     }
     return;
   }
-  // ---- sequence blockIdx.x - H: rotation angles, RoPE queries of every head, cache row --------
+  // ---- sequence: rotation angles, RoPE queries of every head, cache row -------------------------
   __shared__ float cs_c[kMaxHalf], cs_s[kMaxHalf];
   const int eb = p.dtype == 0 ? 2 : 4;
   const int half = p.DR / 2;
-  const int beta = blockIdx.x - p.H;
+  const int beta = blockIdx.x - p.H * ag;
   const int m = p.positions[beta];
-  if (tid < half) rope_cs(m, tid, p.DR, (double)p.rope_base, &cs_c[tid], &cs_s[tid]);
-  __syncthreads();
-  for (int idx = tid; idx < p.H * half; idx += kPrepThreads) {
+  const int nq = p.H * half;                 // RoPE-query pairs of this sequence
+  // The first kQPre query pairs of this thread are loaded before the angles, so that the
+  // loads are in flight while the fp64 angles are computed.
+  float qx0[kQPre], qx1[kQPre];
+#pragma unroll
+  for (int it = 0; it < kQPre; ++it) {
+    const int idx = tid + it * kPrepThreads;
     const int head = idx / half, j = idx - head * half;
     const int64_t o = ((int64_t)beta * p.H + head) * p.DR + 2 * j;
-    const float x0 = ld(p.q_pe, o, p.dtype), x1 = ld(p.q_pe, o + 1, p.dtype);
+    qx0[it] = idx < nq ? ld(p.q_pe, o, p.dtype) : 0.f;
+    qx1[it] = idx < nq ? ld(p.q_pe, o + 1, p.dtype) : 0.f;
+  }
+  if (tid < half) rope_cs(m, tid, p.DR, (double)p.rope_base, &cs_c[tid], &cs_s[tid]);
+  __syncthreads();
+  auto rotate_query = [&](int idx, float x0, float x1) {
+    const int head = idx / half, j = idx - head * half;
+    const int64_t o = ((int64_t)beta * p.H + head) * p.DR + 2 * j;
     st(p.q_rope, o, x0 * cs_c[j] - x1 * cs_s[j], p.dtype);
     st(p.q_rope, o + 1, x0 * cs_s[j] + x1 * cs_c[j], p.dtype);
+  };
+#pragma unroll
+  for (int it = 0; it < kQPre; ++it)
+    if (tid + it * kPrepThreads < nq) rotate_query(tid + it * kPrepThreads, qx0[it], qx1[it]);
+  for (int idx = tid + kQPre * kPrepThreads; idx < nq; idx += kPrepThreads) {
+    const int head = idx / half, j = idx - head * half;
+    const int64_t o = ((int64_t)beta * p.H + head) * p.DR + 2 * j;
+    rotate_query(idx, ld(p.q_pe, o, p.dtype), ld(p.q_pe, o + 1, p.dtype));
   }
   const int per = DC + half;                 // latent elements + RoPE pairs of one row
   for (int e = tid; e < per; e += kPrepThreads) {
@@ -167,7 +196,7 @@ __global__ __launch_bounds__(kPrepThreads) void prepare_kernel(PrepareParams p) 
 bool prepare_mfma_supported(int dh, int dc) { return dh % 32 == 0 && dh <= 32 * kMaxKc && dc % 16 == 0; }
 
 hipError_t launch_prepare(const PrepareParams& p, hipStream_t stream) {
-  hipLaunchKernelGGL(prepare_kernel, dim3(p.H + p.B), dim3(kPrepThreads), 0, stream, p);
+  hipLaunchKernelGGL(prepare_kernel, dim3(p.H * absorb_groups(p) + p.B), dim3(kPrepThreads), 0, stream, p);
   return hipGetLastError();
 }
 
