@@ -251,8 +251,8 @@ def main():
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print(json.dumps({"error": "this build runs on one GPU only: the decode kernel is measured on one "
-                                   "GPU's share; multi-GPU sharding is a design note, not implemented"}))
+        print(json.dumps({"error": "bench.py measures one GPU: the decode kernel runs on one GPU's share of "
+                                   "the work; sharding across GPUs is described but not implemented"}))
         sys.exit(2)
     if args.read_probe:
         print(json.dumps(read_probe()))
