@@ -43,7 +43,7 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 // Work-groups the automatic split count aims for: one per compute unit of an
-// MI355X (256 CUs; the MFMA kernel keeps one 8-wave group per CU).
+// MI355X: 256 CUs, and the MFMA kernel keeps one work-group per CU.
 constexpr int64_t kTargetGroups = 256;
 constexpr int kMaxSplits = 4096;
 constexpr int kPageCache = 256;
