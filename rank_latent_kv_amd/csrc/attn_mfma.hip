@@ -48,6 +48,7 @@ typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4;
 typedef __attribute__((address_space(3))) char lds_char;
 typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) const int lds_cint;
 
 #ifndef MLRA_SUB_PREF
 #define MLRA_SUB_PREF 4
@@ -255,8 +256,12 @@ __global__ __launch_bounds__(W * 64, 1) void attn_mfma_kernel(AttnParams p) {
   auto chunk_src = [&](int c) __attribute__((always_inline)) -> const char* {
     return c >= C::NCL ? seq_rope + (c - C::NCL) * 16 : seq_lat + c * 16;
   };
+  // Paged, pages of at most one stage: `pid_addr` = LDS byte address of the lane's page-id
+  // slot for the split's first stage (a stage adds a uniform offset). The page size in bytes
+  // is below 2^32 (checked on the host), so a page's offset is one 32 x 32 -> 64-bit product.
   const char* dptr[C::DMA_HI];
-  int pslot[C::DMA_HI];
+  uint32_t pid_addr[C::DMA_HI];
+  const uint32_t ptab_lds = (uint32_t)(uintptr_t)(lds_char*)(smem + C::LDS_BYTES - C::PTAB_BYTES);
 #pragma unroll
   for (int i = 0; i < C::DMA_HI; ++i) {
     const DmaLane d = dma_lane(i, lane);
@@ -264,38 +269,51 @@ __global__ __launch_bounds__(W * 64, 1) void attn_mfma_kernel(AttnParams p) {
     if constexpr (PAGED) {
       const int rin = big_pages ? d.tok : (d.tok & pmask);
       dptr[i] = sel + (int64_t)rin * p.row_stride_b;
-      pslot[i] = big_pages ? 0 : (d.tok >> p.page_shift);
+      pid_addr[i] = ptab_lds + 4u * (uint32_t)(big_pages ? 0 : (d.tok >> p.page_shift));
     } else {
       dptr[i] = sel + (int64_t)(t0 + d.tok) * p.row_stride_b;
-      pslot[i] = 0;
+      pid_addr[i] = 0;
     }
   }
   const int64_t page_bytes = PAGED ? ((int64_t)1 << p.page_shift) * p.row_stride_b : 0;
+  const uint32_t page_bytes32 = (uint32_t)page_bytes;
   const int64_t stage_bytes_g = (int64_t)C::ST * p.row_stride_b;
 
   auto issue_stage = [&](int s) __attribute__((always_inline)) {
     const int tok0 = t0 + s * C::ST;
     const uint32_t ring = smem_lds + (uint32_t)((s % C::NS) * C::STAGE_BYTES);
     if (tok0 + C::ST <= t1) {
-      // full stage: one pointer add (and for pages one LDS page-id read) per DMA
+      // full stage: one pointer add (and for small pages one LDS page-id read) per DMA
+      const uint32_t slot0 = ring + (uint32_t)(wave * 1024);
+      if constexpr (PAGED) {
+        if (big_pages) {
+          // one page holds the whole stage: a uniform offset
+          const int pg = __builtin_amdgcn_readfirstlane(ptab[(tok0 >> p.page_shift) - first_page]);
+          const int64_t off = (int64_t)((uint64_t)(uint32_t)pg * page_bytes32) + (int64_t)(tok0 & pmask) * p.row_stride_b;
 #pragma unroll
-      for (int i = 0; i < C::DMA_HI; ++i) {
-        if (i >= ndma) break;
-        const char* src;
-        if constexpr (PAGED) {
-          int pg, rin_extra;
-          if (big_pages) {
-            pg = ptab[(tok0 >> p.page_shift) - first_page];
-            rin_extra = tok0 & pmask;
-          } else {
-            pg = ptab[((tok0 - t0) >> p.page_shift) + pslot[i]];
-            rin_extra = 0;
+          for (int i = 0; i < C::DMA_HI; ++i) {
+            if (i >= ndma) break;
+            dma16(dptr[i] + off, __builtin_amdgcn_readfirstlane(slot0 + (uint32_t)(C::DW * i * 1024)));
           }
-          src = dptr[i] + (int64_t)pg * page_bytes + (int64_t)rin_extra * p.row_stride_b;
         } else {
-          src = dptr[i] + (int64_t)s * stage_bytes_g;
+          // all page ids first (the DMA asm is a compiler barrier for LDS reads), then the DMAs
+          const uint32_t pid_off = 4u * (uint32_t)((tok0 - t0) >> p.page_shift);
+          int pg[C::DMA_HI];
+#pragma unroll
+          for (int i = 0; i < C::DMA_HI; ++i) pg[i] = *(const lds_cint*)(uintptr_t)(pid_addr[i] + pid_off);
+#pragma unroll
+          for (int i = 0; i < C::DMA_HI; ++i) {
+            if (i >= ndma) break;
+            dma16(dptr[i] + (uint64_t)(uint32_t)pg[i] * page_bytes32,
+                  __builtin_amdgcn_readfirstlane(slot0 + (uint32_t)(C::DW * i * 1024)));
+          }
         }
-        dma16(src, __builtin_amdgcn_readfirstlane(ring + (uint32_t)((wave + C::DW * i) * 1024)));
+      } else {
+#pragma unroll
+        for (int i = 0; i < C::DMA_HI; ++i) {
+          if (i >= ndma) break;
+          dma16(dptr[i] + (int64_t)s * stage_bytes_g, __builtin_amdgcn_readfirstlane(slot0 + (uint32_t)(C::DW * i * 1024)));
+        }
       }
     } else {
       // ragged last stage: rows past the end repeat the last row (finite data, masked later).

@@ -169,6 +169,10 @@ mlra_status make_plan(const mlra_decode_args* a, bool check_pointers, Plan* plan
     // the split's page ids must fit the kernel's LDS cache
     const int64_t max_split = (int64_t)(kPageCache - 1) * a->page_size / p.stage * p.stage;
     if (max_split < p.stage) return fail(MLRA_ERR_UNSUPPORTED, "page_size %d too small for the MFMA path", a->page_size);
+    // the kernel forms a page's byte offset as a 32 x 32 -> 64-bit product
+    const int64_t page_bytes = (int64_t)a->page_size * a->row_stride * (a->dtype == MLRA_BF16 ? 2 : 4);
+    if (page_bytes >= ((int64_t)1 << 32))
+      return fail(MLRA_ERR_UNSUPPORTED, "a page of %lld bytes is beyond the MFMA path's 4 GiB limit", (long long)page_bytes);
     split = std::min(split, max_split);
   }
   p.split_tokens = (int)std::min<int64_t>(split, a->max_seq_len + (int64_t)p.stage);

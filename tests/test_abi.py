@@ -209,6 +209,10 @@ def test_paged_validation():
     assert R.validate(a) == R.MLRA_ERR_INVALID_ARG
     a.num_pages = 128
     assert R.validate(a) == R.MLRA_OK
+    # a page of 2^24 rows x 160 bf16 elements is 5 GiB: beyond the 32-bit page offset
+    a.page_size, a.max_pages = 1 << 24, 1
+    assert R.validate(a) == R.MLRA_ERR_UNSUPPORTED
+    assert "4 GiB" in R.last_error()
 
 
 def test_paged_copy_validation():
