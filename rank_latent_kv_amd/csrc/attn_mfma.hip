@@ -1,9 +1,10 @@
 // Split-context flash-decode attention for MLRA / MLA on gfx950 (bf16 inputs,
 // fp32 accumulation, MFMA 32x32x16).
 //
-// One work-group of W waves (16 for MLRA-4, 8 for the single-latent shapes) owns one
-// (sequence, context split). The split's cache rows stream HBM -> LDS once, through a
-// ring of up to four stages filled by asynchronous LDS-DMA loads, and every query head
+// One work-group of W waves (16 for MLRA-4, 8 for most single-latent shapes, 4 for the
+// 16-head MLA shard) owns one (sequence, context split). The split's cache rows stream
+// HBM -> LDS once, through a ring of as many stages as fit in LDS (at most eight) filled by
+// asynchronous LDS-DMA loads, and every query head
 // reads them from LDS: all heads share one cached latent (MLRA page
 // "原生支持张量并行的多分支低秩注意力MLRA", §1.3 step 2, MQA-style attention over the
 // latent; §3.1, each branch attends over its own latent block plus the RoPE key shared
