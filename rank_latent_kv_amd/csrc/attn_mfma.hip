@@ -250,8 +250,7 @@ __global__ __launch_bounds__(W * 64, 1) void attn_mfma_kernel(AttnParams p) {
   const char* seq_rope = p.kv_rope + (PAGED ? 0 : (int64_t)beta * p.seq_stride_b);
   // Per-lane source pointers of full stages. Contiguous: the lane's row of stage 0
   // of this split (later stages add s * ST rows). Paged: the lane's row inside its
-  // page (the page base is added per stage); pages of at most one stage hold
-  // `pslot` = the lane's page index inside the stage.
+  // page (the page base is added per stage).
   const int pmask = PAGED ? (1 << p.page_shift) - 1 : 0;
   const bool big_pages = PAGED && (1 << p.page_shift) > C::ST;
   auto chunk_src = [&](int c) __attribute__((always_inline)) -> const char* {
