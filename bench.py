@@ -6,7 +6,9 @@ A step is one full decode call of the library, the attention kernel over
 context splits plus the split merge with the W^V epilogue, over one batch of
 synthetic input already resident in HBM. Timed steps rotate among enough
 identical copies of the cache (>= 512 MiB in total) that the 256 MiB Infinity
-Cache cannot serve them. The one JSON line reports decoded tokens/s (batch /
+Cache cannot serve them. The default warm-up (2000 steps, about 0.1 s at the
+headline) outlasts the GPU's clock ramp under sustained load, so the timed steps
+see its steady state. The one JSON line reports decoded tokens/s (batch /
 step time), the attention kernel's achieved HBM bandwidth (HIP events recorded
 by the library around that kernel, on its stream, on every 16th timed call so
 that the events do not slow the timed calls) against the 8 TB/s peak, and the
@@ -190,18 +192,18 @@ def reduce_pmc(workload: str, fetch_csv: str, write_csv: str, command: str) -> s
     return "\n".join(lines) + "\n"
 
 
-def read_probe(sizes=(167_772_160, 536_870_912), calls=50):
+def read_probe(sizes=(167_772_160, 536_870_912), calls=400, warmup=2000):
     """The box's practical streaming-read rate: the library's read probe (one coalesced
     stream of 16-byte nontemporal loads) over buffers of the headline and TP-shard cache
     sizes, rotating enough copies (>= 512 MiB) that the Infinity Cache cannot serve them,
-    timed with events around all calls."""
+    timed with events around all calls after a warm-up as long as the decode bench's."""
     dev = torch.device("cuda:0")
     res = []
     for nbytes in sizes:
         copies = max(1, math.ceil(ROTATE_BYTES / nbytes))
         bufs = [torch.ones(nbytes // 4, dtype=torch.int32, device=dev) for _ in range(copies)]
         out = torch.empty(int(R.lib().mlra_read_probe_words()), dtype=torch.int32, device=dev)
-        for k in range(5):
+        for k in range(warmup):
             R.read_probe(bufs[k % copies], out)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
@@ -221,7 +223,9 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=400)
-    ap.add_argument("--warmup", type=int, default=40)
+    ap.add_argument("--warmup", type=int, default=2000,
+                    help="untimed steps first: under back-to-back decode calls the GPU takes some 25-30 ms "
+                         "(about 500 headline calls) to settle its clocks, and shorter warm-ups time that ramp")
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(PRESETS))
     ap.add_argument("--num-splits", type=int, default=0)
     ap.add_argument("--batch", type=int, default=0, help="override the workload's batch (reported in config)")
