@@ -566,8 +566,11 @@ __global__ __launch_bounds__(W * 64, 1) void attn_mfma_kernel(AttnParams p) {
   // the softmax of sub-tile k, so the matrix cores work while the vector ALUs
   // exponentiate. A ring slot is still read by the lagging P.C of its last sub-tile after
   // the next stage's barrier, so the refill at stage s's barrier targets the slot of stage
-  // s - 2: LOOK = NS - 2 stages ahead (kept for the unpipelined loop too).
-  constexpr int LOOK = C::NS - 2;
+  // s - 2: LOOK = NS - 2 stages ahead. Without the pipelining every wave is done with stage
+  // s - 1 when it passes stage s's barrier, so any slot but stage s's may be refilled; two
+  // stages ahead measured best there (three ahead was slower on a 4-stage ring, one ahead
+  // much slower on the 3-stage ring of the paged instance).
+  constexpr int LOOK = C::PIPE ? C::NS - 2 : 2;
   for (int s = 0; s < LOOK && s < nst; ++s) issue_stage(s);
   auto begin_piped = [&](int s) __attribute__((always_inline)) {
     const int ahead = min(nst - 1 - s, LOOK - 1);
@@ -730,11 +733,11 @@ __global__ __launch_bounds__(W * 64, 1) void attn_mfma_kernel(AttnParams p) {
   }
 }
 
-template <int NB, int DB, int DR, int HEADS, int W, int BPW, int BPW_PAGED>
+template <int NB, int DB, int DR, int HEADS, int W, int BPW>
 hipError_t launch_shape(const AttnParams& p, bool paged, int grid_splits, hipStream_t stream) {
   dim3 grid(grid_splits, p.B);
   if (paged)
-    hipLaunchKernelGGL((attn_mfma_kernel<NB, DB, DR, HEADS, W, true, BPW_PAGED>), grid, dim3(W * 64), 0, stream, p);
+    hipLaunchKernelGGL((attn_mfma_kernel<NB, DB, DR, HEADS, W, true, BPW>), grid, dim3(W * 64), 0, stream, p);
   else
     hipLaunchKernelGGL((attn_mfma_kernel<NB, DB, DR, HEADS, W, false, BPW>), grid, dim3(W * 64), 0, stream, p);
   return hipGetLastError();
@@ -743,24 +746,19 @@ hipError_t launch_shape(const AttnParams& p, bool paged, int grid_splits, hipStr
 }  // namespace
 
 // Shapes built with the MFMA path: (branches, branch width, RoPE width, heads, waves,
-// branches per wave for a contiguous cache, for a paged cache). Two branches per wave share
-// the RoPE score. The paged MLRA-4 instance keeps one branch per wave: with two, its page
-// bookkeeping leaves the registers so short that the compiler adds copies to the loop and
-// it runs slower than with one. (Instances with different values sum the tokens of a split
-// in a different order, so paged and contiguous results then differ by rounding.)
-#ifndef MLRA4_BPW
-#define MLRA4_BPW 2
-#endif
-#define MLRA_MFMA_SHAPES(X)            \
-  X(4, 32, 32, 64, 16, MLRA4_BPW, 1)   \
-  X(1, 128, 32, 64, 8, 1, 1)           \
-  X(1, 128, 32, 16, 4, 1, 1)           \
-  X(1, 32, 32, 16, 8, 1, 1)            \
-  X(1, 32, 32, 64, 8, 1, 1)            \
-  X(2, 64, 32, 64, 8, 1, 1)
+// branches per wave). Two branches per wave share the RoPE score. The contiguous and paged
+// instances of a shape split the work identically, so they sum every split's tokens in the
+// same order and agree bit for bit.
+#define MLRA_MFMA_SHAPES(X)     \
+  X(4, 32, 32, 64, 16, 2)       \
+  X(1, 128, 32, 64, 8, 1)       \
+  X(1, 128, 32, 16, 4, 1)       \
+  X(1, 32, 32, 16, 8, 1)        \
+  X(1, 32, 32, 64, 8, 1)        \
+  X(2, 64, 32, 64, 8, 1)
 
 int mfma_stage_tokens(int nb, int db, int dr, int heads) {
-#define X(xNB, xDB, xDR, xH, xW, xBPW, xBPWP) \
+#define X(xNB, xDB, xDR, xH, xW, xBPW) \
   if (nb == xNB && db == xDB && dr == xDR && heads == xH) return Cfg<xNB, xDB, xDR, xH, xW, false, xBPW>::ST;
   MLRA_MFMA_SHAPES(X)
 #undef X
@@ -768,9 +766,9 @@ int mfma_stage_tokens(int nb, int db, int dr, int heads) {
 }
 
 hipError_t launch_attn_mfma(const AttnParams& p, bool paged, int grid_splits, hipStream_t stream) {
-#define X(xNB, xDB, xDR, xH, xW, xBPW, xBPWP) \
+#define X(xNB, xDB, xDR, xH, xW, xBPW) \
   if (p.NB == xNB && p.DB == xDB && p.DR == xDR && p.H == xH) \
-    return launch_shape<xNB, xDB, xDR, xH, xW, xBPW, xBPWP>(p, paged, grid_splits, stream);
+    return launch_shape<xNB, xDB, xDR, xH, xW, xBPW>(p, paged, grid_splits, stream);
   MLRA_MFMA_SHAPES(X)
 #undef X
   return hipErrorInvalidValue;
