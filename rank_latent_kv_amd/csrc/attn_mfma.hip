@@ -34,6 +34,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <type_traits>
 
 #include "mlra_internal.h"
 
@@ -94,7 +95,7 @@ struct Cfg {
   static constexpr int MT = DB / 32;                     // value M-tiles (32 features)
   static constexpr int KR = DR / 16;                     // RoPE K-chunks of the score
   static constexpr int KL = DB / 16;                     // latent K-chunks of the score
-  static constexpr int MERGE_WAVES = W - NBG * HGSPLIT;
+  static constexpr int MERGE_WAVES = P > 1 ? W : 0;     // every wave publishes a merge record
   static constexpr int MERGE_FLOATS = HPW * BPW * (16 * MT + 2) * 64;   // per wave record
   static constexpr int PTAB_BYTES = PAGED ? kPageCache * 4 : 0;
   static constexpr int NS_FIT = (kLdsBytes - PTAB_BYTES) / STAGE_BYTES;
@@ -167,6 +168,16 @@ __device__ __forceinline__ void wait_dma(int ahead) {
 }
 
 __device__ __forceinline__ void block_barrier() { asm volatile("s_barrier" : : : "memory"); }
+
+// f(std::integral_constant<int, v>) for the runtime value v in [0, N): a wave-uniform branch
+// to code in which v is a compile-time constant (so register arrays are indexed statically).
+template <int N, class F>
+__device__ __forceinline__ void static_phase(int v, F&& f) {
+  if constexpr (N > 0) {
+    if (v == N - 1) f(std::integral_constant<int, N - 1>{});
+    else static_phase<N - 1>(v, f);
+  }
+}
 
 // Max and sum of the values held by lanes l and l ^ 32 (the two lanes holding the two
 // 16-token halves of one head's column). v_permlane32_swap with the same register as both
@@ -658,78 +669,118 @@ __global__ __launch_bounds__(W * 64, 1) void attn_mfma_kernel(AttnParams p) {
 #pragma unroll
     for (int bb = 0; bb < BPW; ++bb) lsum[h][bb] = halves_sum(lsum[h][bb]);
 
+  // Rows [r0, r0 + nr) of every output tile of this wave, and (with ml) its (m, l), into the
+  // split's record. A lane's rows 4j..4j+3 are 4 consecutive features.
+  auto store_rows = [&](int r0, int nr, bool ml) __attribute__((always_inline)) {
+#pragma unroll
+    for (int h = 0; h < C::HPW; ++h) {
+      const int head = (hgslot * C::HPW + h) * 32 + n32;
+      if (head >= p.H) continue;
+#pragma unroll
+      for (int bb = 0; bb < BPW; ++bb) {
+        const int64_t rec = (((int64_t)beta * p.num_splits + split) * p.H + head) * NB + bg * BPW + bb;
+        float* o = p.ws_o + rec * DB;
+#pragma unroll
+        for (int mt = 0; mt < C::MT; ++mt) {
+          if (nr >= 4) {
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+              if (q4 < r0 / 4 || q4 >= (r0 + nr) / 4) continue;
+              *reinterpret_cast<float4*>(o + 32 * mt + 8 * q4 + 4 * g) =
+                  make_float4(acc[h][bb][mt][4 * q4], acc[h][bb][mt][4 * q4 + 1], acc[h][bb][mt][4 * q4 + 2],
+                              acc[h][bb][mt][4 * q4 + 3]);
+            }
+          } else {
+#pragma unroll
+            for (int r = 0; r < 16; r += 2) {
+              if (r != r0) continue;
+              *reinterpret_cast<float2*>(o + 32 * mt + 8 * (r / 4) + 4 * g + (r % 4)) =
+                  make_float2(acc[h][bb][mt][r], acc[h][bb][mt][r + 1]);
+            }
+          }
+        }
+        if (ml && g == 0) {
+          p.ws_ml[rec * 2] = mref[h][bb];
+          p.ws_ml[rec * 2 + 1] = lsum[h][bb];
+        }
+      }
+    }
+  };
+
   if constexpr (C::P > 1) {
+    // The P phase waves of a (branch group, head group) merge their states through LDS, each
+    // finalising 16 / P of the 16 rows a lane holds per output tile, and write those rows.
+    constexpr int RP = 16 / C::P;
+    static_assert(16 % C::P == 0 && RP >= 2, "phases split a lane's 16 output rows");
     block_barrier();   // every wave is done with the ring; reuse it for the merge records
     float* rec = reinterpret_cast<float*>(smem);
     constexpr int RECF = (16 * C::MT + 2) * 64;     // floats of one (head group, branch) record
-    auto slot_of = [&](int q) __attribute__((always_inline)) {
-      return bg * (C::WPB - C::HGSPLIT) + (q - 1) * C::HGSPLIT + hgslot;
-    };
-    if (phase > 0) {
-      float* dst = rec + slot_of(phase) * C::MERGE_FLOATS;
+    auto slot_of = [&](int q) __attribute__((always_inline)) { return bg * C::WPB + q * C::HGSPLIT + hgslot; };
+    // 1. publish the rows the other phases finalise, and (m, l)
+    auto publish = [&](auto pc) __attribute__((always_inline)) {
+      constexpr int R0 = decltype(pc)::value * RP;
+      float* mine = rec + wave * C::MERGE_FLOATS;
 #pragma unroll
       for (int h = 0; h < C::HPW; ++h)
 #pragma unroll
         for (int bb = 0; bb < BPW; ++bb) {
-          float* d = dst + (h * BPW + bb) * RECF;
+          float* d = mine + (h * BPW + bb) * RECF;
 #pragma unroll
           for (int mt = 0; mt < C::MT; ++mt)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) d[(16 * mt + r) * 64 + lane] = acc[h][bb][mt][r];
+            for (int r = 0; r < 16; ++r)
+              if (r < R0 || r >= R0 + RP) d[(16 * mt + r) * 64 + lane] = acc[h][bb][mt][r];
           d[(16 * C::MT) * 64 + lane] = mref[h][bb];
           d[(16 * C::MT + 1) * 64 + lane] = lsum[h][bb];
         }
-    }
-    __syncthreads();
-    if (phase > 0) return;
+    };
+    // 2. merge this wave's rows over the phases and write them
+    auto finish = [&](auto pc) __attribute__((always_inline)) {
+      constexpr int PH = decltype(pc)::value;
+      constexpr int R0 = PH * RP;
 #pragma unroll
-    for (int h = 0; h < C::HPW; ++h)
+      for (int h = 0; h < C::HPW; ++h)
 #pragma unroll
-      for (int bb = 0; bb < BPW; ++bb) {
-        float mstar = mref[h][bb];
-        for (int q = 1; q < C::P; ++q) {
-          const float* d = rec + slot_of(q) * C::MERGE_FLOATS + (h * BPW + bb) * RECF;
-          mstar = fmaxf(mstar, d[(16 * C::MT) * 64 + lane]);
-        }
-        const float f0 = __builtin_amdgcn_exp2f(mref[h][bb] - mstar);
-        float l = lsum[h][bb] * f0;
+        for (int bb = 0; bb < BPW; ++bb) {
+          float mq[C::P];
+          float mstar = mref[h][bb];
 #pragma unroll
-        for (int mt = 0; mt < C::MT; ++mt) acc[h][bb][mt] *= f0;
-        for (int q = 1; q < C::P; ++q) {
-          const float* d = rec + slot_of(q) * C::MERGE_FLOATS + (h * BPW + bb) * RECF;
-          const float fq = __builtin_amdgcn_exp2f(d[(16 * C::MT) * 64 + lane] - mstar);
-          l += d[(16 * C::MT + 1) * 64 + lane] * fq;
+          for (int q = 0; q < C::P; ++q) {
+            if (q == PH) continue;
+            mq[q] = rec[slot_of(q) * C::MERGE_FLOATS + (h * BPW + bb) * RECF + (16 * C::MT) * 64 + lane];
+            mstar = fmaxf(mstar, mq[q]);
+          }
+          // the phases in order 0 .. P-1, whichever wave finalises the rows
+          float l = 0.f;
+          float o[C::MT][RP];
+#pragma unroll
+          for (int q = 0; q < C::P; ++q) {
+            const float* d = rec + slot_of(q) * C::MERGE_FLOATS + (h * BPW + bb) * RECF;
+            const float fq = __builtin_amdgcn_exp2f((q == PH ? mref[h][bb] : mq[q]) - mstar);
+            const float lq = q == PH ? lsum[h][bb] : d[(16 * C::MT + 1) * 64 + lane];
+            l = q == 0 ? lq * fq : l + lq * fq;
+#pragma unroll
+            for (int mt = 0; mt < C::MT; ++mt)
+#pragma unroll
+              for (int r = 0; r < RP; ++r) {
+                const float v = q == PH ? acc[h][bb][mt][R0 + r] : d[(16 * mt + R0 + r) * 64 + lane];
+                o[mt][r] = q == 0 ? v * fq : o[mt][r] + v * fq;
+              }
+          }
 #pragma unroll
           for (int mt = 0; mt < C::MT; ++mt)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) acc[h][bb][mt][r] += d[(16 * mt + r) * 64 + lane] * fq;
+            for (int r = 0; r < RP; ++r) acc[h][bb][mt][R0 + r] = o[mt][r];
+          mref[h][bb] = mstar;
+          lsum[h][bb] = l;
         }
-        mref[h][bb] = mstar;
-        lsum[h][bb] = l;
-      }
-  }
-
-#pragma unroll
-  for (int h = 0; h < C::HPW; ++h) {
-    const int head = (hgslot * C::HPW + h) * 32 + n32;
-    if (head >= p.H) continue;
-#pragma unroll
-    for (int bb = 0; bb < BPW; ++bb) {
-      const int64_t rec = (((int64_t)beta * p.num_splits + split) * p.H + head) * NB + bg * BPW + bb;
-      float* o = p.ws_o + rec * DB;
-#pragma unroll
-      for (int mt = 0; mt < C::MT; ++mt)
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          float4 v = make_float4(acc[h][bb][mt][4 * q4], acc[h][bb][mt][4 * q4 + 1], acc[h][bb][mt][4 * q4 + 2],
-                                 acc[h][bb][mt][4 * q4 + 3]);
-          *reinterpret_cast<float4*>(o + 32 * mt + 8 * q4 + 4 * g) = v;
-        }
-      if (g == 0) {
-        p.ws_ml[rec * 2] = mref[h][bb];
-        p.ws_ml[rec * 2 + 1] = lsum[h][bb];
-      }
-    }
+      store_rows(R0, RP, PH == 0);
+    };
+    static_phase<C::P>(phase, publish);
+    __syncthreads();
+    static_phase<C::P>(phase, finish);
+  } else {
+    store_rows(0, 16, true);
   }
 }
 
