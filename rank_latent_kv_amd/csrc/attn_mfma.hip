@@ -52,11 +52,8 @@ typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef __attribute__((address_space(3))) const int lds_cint;
 
-#ifndef MLRA_SUB_PREF
-#define MLRA_SUB_PREF 4
-#endif
-
 constexpr int kMaxStages = 8;
+constexpr int kSubPerStage = 4;            // 32-token sub-tiles per stage (more when there are more phases)
 constexpr int kLdsBytes = 160 * 1024;
 constexpr int kPageCache = 256;            // page ids of one split kept in LDS (paged mode)
 constexpr float kRescaleThreshold = 8.0f;  // log2 units: p = 2^x stays <= 256
@@ -72,7 +69,7 @@ struct Cfg {
   static constexpr int HGSPLIT = WPB < NHG ? WPB : NHG;  // head-group slots per branch group
   static constexpr int HPW = NHG / HGSPLIT;              // head groups per wave
   static constexpr int P = WPB / HGSPLIT;                // token phases
-  static constexpr int SUB = P > MLRA_SUB_PREF ? P : MLRA_SUB_PREF;   // 32-token sub-tiles per stage
+  static constexpr int SUB = P > kSubPerStage ? P : kSubPerStage;     // 32-token sub-tiles per stage
   static constexpr int NSW = SUB / P;                    // sub-tiles of one wave per stage
   // one branch per wave: the next sub-tile's scores are issued before the current softmax;
   // with several branches per wave their score tiles leave no registers for that
