@@ -110,6 +110,27 @@ def test_peaked_logits(preset, mla):
     assert err <= TOL_BF16
 
 
+@pytest.mark.parametrize("offset", [-300.0, 300.0])
+@pytest.mark.parametrize("preset,mla", [("mlra4_b16_l32k", False), ("mla_b16_l32k", True)])
+def test_logit_offset(offset, preset, mla):
+    """Adding one constant to every logit of a head leaves its softmax unchanged. Here the
+    RoPE key is the same vector for every token, so q^R . k^R shifts all logits by `offset`
+    (natural-log units): far past where exp over- or underflows in fp32 unless a reference
+    max is subtracted. The oracle subtracts the exact max in fp64."""
+    lens = [3000, 700]
+    w = PRESETS[preset].replace(batch=len(lens))
+    inp = make_inputs(w, seq_lens=lens)
+    dc, k0 = w.latent_dim, 16.0
+    kv = inp["kv"].float()
+    kv[..., dc:] = 0.0
+    kv[..., dc] = k0
+    q_rope = torch.zeros(inp["q_rope"].shape)
+    q_rope[..., 0] = offset / (w.sm_scale * k0)
+    inp = dict(inp, kv=kv.to(inp["kv"].dtype), q_rope=q_rope.to(inp["q_rope"].dtype))
+    say(f"logit offset {offset} {preset}")
+    check(w, inp, mla=mla)
+
+
 def test_split_invariance():
     w = PRESETS["mlra4_b16_l32k"].replace(batch=2)
     inp = make_inputs(w, seq_lens=[3000, 2900])
