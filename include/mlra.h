@@ -297,9 +297,10 @@ void mlra_page_pool_destroy(mlra_page_pool* pool);
 
 /*
  * Measurement support: a streaming-read probe. Reads the `bytes` bytes at device
- * pointer `src` once, as one coalesced stream of 16-byte nontemporal loads, so that a
- * caller can time the read rate this GPU reaches (the practical ceiling next to the
- * HBM peak, for reading the attention kernel's achieved bandwidth). Writes
+ * pointer `src` once with 16-byte nontemporal loads, each work-group streaming one
+ * contiguous chunk, so that a caller can time the read rate this GPU reaches (the
+ * practical ceiling next to the HBM peak, for reading the attention kernel's achieved
+ * bandwidth). Writes
  * mlra_read_probe_words() 32-bit words to device buffer `out`: out[g] is the XOR of
  * the 32-bit words read by work-group g, so the XOR of all of them equals the XOR of
  * every 32-bit word of the buffer. Enqueued on `stream` without waiting.

@@ -76,7 +76,7 @@ hipError_t launch_merge(const MergeParams& p, hipStream_t stream);
 
 // Streaming-read probe (measurement support): kProbeBlocks work-groups of kProbeThreads
 // threads; out[g] = XOR of the 32-bit words work-group g read.
-constexpr int kProbeBlocks = 4096;
+constexpr int kProbeBlocks = 2048;
 constexpr int kProbeThreads = 256;
 hipError_t launch_read_probe(const void* src, int64_t bytes, uint32_t* out, hipStream_t stream);
 

@@ -1,8 +1,10 @@
 // Streaming-read probe: the HBM read rate this GPU actually reaches with a plain
 // coalesced stream, the practical ceiling next to the 8 TB/s peak for judging the
-// attention kernel's bandwidth. Every 16-byte word of the buffer is read once with a
-// nontemporal load; each work-group writes the XOR of the 32-bit words it read, so the
-// loads cannot be dropped and the host can check the result bit for bit.
+// attention kernel's bandwidth. Work-group g reads the g-th of kProbeBlocks contiguous
+// chunks of the buffer, 16-byte nontemporal loads with four in flight per thread, so
+// each group streams through consecutive DRAM pages. Every 16-byte word is read once;
+// each work-group writes the XOR of the 32-bit words it read, so the loads cannot be
+// dropped and the host can check the result bit for bit.
 #include <hip/hip_runtime.h>
 
 #include "mlra_internal.h"
@@ -14,19 +16,21 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 __global__ __launch_bounds__(kProbeThreads) void read_probe_kernel(const u32x4* __restrict__ src, int64_t n16,
                                                                     uint32_t* __restrict__ out) {
-  const int64_t stride = (int64_t)gridDim.x * kProbeThreads;
-  int64_t i = (int64_t)blockIdx.x * kProbeThreads + threadIdx.x;
+  const int64_t per = (n16 + gridDim.x - 1) / gridDim.x;
+  const int64_t b0 = (int64_t)blockIdx.x * per;
+  const int64_t b1 = b0 + per < n16 ? b0 + per : n16;
+  constexpr int T = kProbeThreads;
+  int64_t i = b0 + threadIdx.x;
   uint32_t acc = 0;
-  // four independent loads in flight per thread per trip
-  for (; i + 3 * stride < n16; i += 4 * stride) {
+  for (; i + 3 * T < b1; i += 4 * T) {
     const u32x4 a = __builtin_nontemporal_load(src + i);
-    const u32x4 b = __builtin_nontemporal_load(src + i + stride);
-    const u32x4 c = __builtin_nontemporal_load(src + i + 2 * stride);
-    const u32x4 d = __builtin_nontemporal_load(src + i + 3 * stride);
+    const u32x4 b = __builtin_nontemporal_load(src + i + T);
+    const u32x4 c = __builtin_nontemporal_load(src + i + 2 * T);
+    const u32x4 d = __builtin_nontemporal_load(src + i + 3 * T);
     const u32x4 x = a ^ b ^ c ^ d;
     acc ^= x.x ^ x.y ^ x.z ^ x.w;
   }
-  for (; i < n16; i += stride) {
+  for (; i < b1; i += T) {
     const u32x4 a = __builtin_nontemporal_load(src + i);
     acc ^= a.x ^ a.y ^ a.z ^ a.w;
   }
