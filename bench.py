@@ -73,6 +73,19 @@ def setup(w, inp, dev, copies):
     return d, caches
 
 
+def event_schedule(steps: int, event_every: int):
+    """Which timed calls carry the attention kernel's events: calls k with
+    k % every == phase, n_samples of them, sample j at call phase + j * every.
+
+    The samples sit mid-period (every/2, every/2 + every, ...): the first call after the host
+    synchronisation that opens the timed region starts on an idle GPU and runs 5-25 us slower
+    than the steady calls, a boundary effect of the timing rather than kernel work. Runs too
+    short for that start at call 0."""
+    every = max(1, event_every)
+    phase = every // 2 if steps > every // 2 else 0
+    return every, phase, len(range(phase, steps, every))
+
+
 def make_step_args(w, d, cache, out, ws, lens_host, events=None):
     dc = w.latent_dim
     kv_lat, kv_rope = cache[..., :dc], cache[..., dc:]
@@ -291,13 +304,9 @@ def main():
     K, W = args.steps, args.warmup
     # HIP events around the attention kernel of every event_every-th call: a pair on every call adds
     # about 5 us to each call's wall time, so the timed calls are sampled evenly instead
-    every = max(1, args.event_every)
-    # Samples sit mid-period (calls every/2, every/2 + every, ...): the first call after the
-    # host synchronisation that opens the timed region starts on an idle GPU and runs 5-25 us
-    # slower than the steady calls, a boundary effect of the timing rather than kernel work.
-    phase = every // 2 if K > every // 2 else 0
+    every, phase, n_samples = event_schedule(K, args.event_every)
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(phase, K, every)]
+           for _ in range(n_samples)]
     for e0, e1 in evs:      # materialise the HIP events so the library can record them
         e0.record()
         e1.record()
