@@ -48,6 +48,14 @@ def test_benchmark_workload_full_size(preset, mla, seqs):
     check_sampled(w, inp, seqs, mla=mla)
 
 
+def test_peaked_logits_at_full_length():
+    """Planted dominant logits over whole 32k contexts: the running-max rescales and the split
+    merge at the benchmark's launch configuration."""
+    w = PRESETS["mlra4_b16_l32k"].replace(batch=4, name="mlra4_b4_l32k_peaked")
+    say("peaked logits, 4 x 32768 tokens")
+    check_sampled(w, make_inputs(w, peaked=True), [0, 1, 2, 3])
+
+
 def test_single_context_of_a_million_tokens():
     w = PRESETS["mlra4_b16_l32k"].replace(batch=1, seq_len=1 << 20, name="mlra4_b1_l1m")
     say("single 2^20-token context")
