@@ -27,6 +27,31 @@ def test_paged_decode_matches_oracle():
     assert err <= 1e-2
 
 
+@pytest.mark.parametrize("num_splits", [1, 3, 8])
+def test_paged_split_invariance(num_splits):
+    """Explicit split counts through the page table: splits start on page boundaries of any
+    count, and the result stays within the bf16 bound of the oracle."""
+    w, inp = small_paged([3000, 9000, 64, 4097])
+    say(f"paged num_splits={num_splits}")
+    y = f64(gpu_decode(w, inp, num_splits=num_splits, out_dtype=torch.float32))
+    err = row_rel_err(y, oracle_decode(w, inp))
+    say(f"paged num_splits={num_splits} err {err:.3e}")
+    assert err <= 1e-2
+
+
+@pytest.mark.parametrize("page_size", [32, 256])
+def test_paged_mla(page_size):
+    """The single-latent kernel through a page table of other page sizes."""
+    w = PRESETS["mlra4_paged_b4_l64k_128k"].replace(batch=3, branches=1, branch_dim=128, page_size=page_size,
+                                                      name=f"mla_paged_ps{page_size}")
+    inp = make_inputs(w, seq_lens=[2500, 700, 4096])
+    say(f"mla paged page_size={page_size}")
+    y = f64(gpu_decode(w, inp, mla=True))
+    err = row_rel_err(y, oracle_decode(w, inp))
+    say(f"mla paged page_size={page_size} err {err:.3e}")
+    assert err <= 1e-2
+
+
 def test_paged_peaked():
     w, inp = small_paged([5000, 2048], peaked=True)
     say("paged peaked")

@@ -82,6 +82,20 @@ def test_mla_tp_shard_16_heads(lens):
     check(w, make_inputs(w, seq_lens=lens), mla=True)
 
 
+@pytest.mark.parametrize("lens", [[1, 33, 129, 2049]])
+def test_mlra2_bf16_ragged(lens):
+    w = PRESETS["mlra2_b16_l32k"].replace(batch=len(lens))
+    say(f"mlra2 bf16 lens={lens}")
+    check(w, make_inputs(w, seq_lens=lens))
+
+
+@pytest.mark.parametrize("preset,mla", [("mlra4_tp_shard_b64_l64k", False), ("mla_tp_shard_b64_l64k", True)])
+def test_tp_shard_fp32_output(preset, mla):
+    w = PRESETS[preset].replace(batch=3)
+    say(f"{preset} fp32 out")
+    check(w, make_inputs(w, seq_lens=[3000, 257, 1]), mla=mla, out_dtype=torch.float32)
+
+
 @pytest.mark.parametrize("nb,db,heads", [(1, 32, 64), (2, 64, 64)])
 def test_other_mfma_shapes(nb, db, heads):
     w = PRESETS["mlra4_b16_l32k"].replace(batch=2, branches=nb, branch_dim=db, heads=heads, name=f"nb{nb}_db{db}")
