@@ -82,7 +82,9 @@ typedef enum mlra_dtype { MLRA_BF16 = 0, MLRA_F32 = 1 } mlra_dtype;
  *             (1 <= seq_lens[beta] <= max_seq_len). Values outside that range are
  *             clamped on the device and reported in *error_flags.
  *   seq_lens_host optional host copy of seq_lens; when given it is validated
- *             (an empty context is rejected, the softmax of no tokens is undefined).
+ *             (an empty context is rejected, the softmax of no tokens is undefined)
+ *             and the automatic split is sized from the real lengths, so that every
+ *             shader engine holds at most one working group per CU (one pass).
  *   max_seq_len host upper bound on every seq_lens entry; sizes the launch.
  *   page_table device int32 [B][max_pages] or NULL; page_size must be a power of
  *             two; num_pages = rows of the pool / page_size (entries outside

@@ -336,6 +336,48 @@ def test_auto_split_fits_one_pass_over_the_cus():
     assert groups <= 256
 
 
+def _auto_split_tokens(lens):
+    """The automatic split of an MLRA-4 headline-shaped launch, read back from the workspace
+    size (one record of 32 fp32 outputs and an (m, l) pair per sequence, split, head, branch)."""
+    a = base_args(B=len(lens), L=max(lens), lens=lens)
+    recs_per_split = len(lens) * 64 * 4
+    splits = R.workspace_size(a) // (recs_per_split * 32 * 4 + recs_per_split * 2 * 4)
+    return splits, -(-max(lens) // splits)
+
+
+def _working_groups_per_engine(lens, splits, split_tokens):
+    """Work-groups that hold tokens on each shader engine, for the (splits, batch) grid placed
+    as MI355X places it: linear id mod 8 picks the XCD, then (id / 8) mod 4 the engine."""
+    split = -(-split_tokens // 128) * 128
+    count = {}
+    for b, L in enumerate(lens):
+        s = 0
+        while s * split < L:
+            i = b * splits + s
+            key = (i % 8, (i // 8) % 4)
+            count[key] = count.get(key, 0) + 1
+            s += 1
+    return count
+
+
+@pytest.mark.parametrize("lens,expect", [
+    ([84575, 128735, 91988, 118737], 1792),        # the paged workload's lengths
+    ([32768] * 16, 2048),                          # the headline: 256 groups, no empty ones
+    ([16271, 41432, 23455, 72937, 107740, 66915, 69898, 93405, 57756, 111379, 35519, 20302], 4096),
+    ([27772, 59750, 93319, 14328, 17494, 78239], 1280),
+    ([12914, 19265, 64838, 62810], 768),
+])
+def test_auto_split_runs_one_pass_per_shader_engine(lens, expect):
+    """The automatic split grows until no shader engine (8 CUs, one group each) gets a ninth
+    group that holds tokens. On the last three batches a split chosen by the total group count
+    alone (2944, 1152 and 640 tokens) puts nine on some engine, which measured 30% slower."""
+    splits, split_tokens = _auto_split_tokens(lens)
+    assert splits == -(-max(lens) // expect)
+    count = _working_groups_per_engine(lens, splits, split_tokens)
+    assert sum(count.values()) <= 256
+    assert max(count.values()) <= 8
+
+
 # ---- the prepare step ------------------------------------------------------------------------
 
 def test_prepare_struct_layout_matches_header():
