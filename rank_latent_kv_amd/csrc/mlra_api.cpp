@@ -188,7 +188,22 @@ mlra_status make_plan(const mlra_decode_args* a, bool check_pointers, Plan* plan
   if (mfma && a->num_splits == 0) {
     // Ragged lengths round up per sequence, which can leave a few work-groups beyond
     // one per CU, or more than one per CU on one shader engine; those would run as a
-    // second pass. Grow the split one stage at a time until the groups fit a single pass.
+    // second pass. The group count only falls as the split grows, so the smallest split
+    // (in whole stages) whose groups fit one per CU is found by bisection; from there the
+    // split grows one stage at a time until no shader engine gets a ninth group.
+    if (split < a->max_seq_len && count_groups(a, split) > kTargetGroups) {
+      int64_t lo = split / p.stage, hi = cdiv(a->max_seq_len, p.stage);   // count(hi) is the batch size
+      if (count_groups(a, hi * p.stage) > kTargetGroups) {
+        lo = hi;                                      // more sequences than CUs: one split each
+      } else {
+        while (lo < hi) {
+          const int64_t mid = lo + (hi - lo) / 2;
+          if (count_groups(a, mid * p.stage) > kTargetGroups) lo = mid + 1;
+          else hi = mid;
+        }
+      }
+      split = lo * p.stage;
+    }
     while (split < a->max_seq_len && (count_groups(a, split) > kTargetGroups || !one_pass_per_engine(a, split)))
       split += p.stage;
   }
