@@ -1,8 +1,8 @@
 // Split-context flash-decode attention for MLRA / MLA on gfx950 (bf16 inputs,
 // fp32 accumulation, MFMA 32x32x16).
 //
-// One work-group of W waves (16 for MLRA-4, 8 for most single-latent shapes, 4 for the
-// 16-head MLA shard) owns one (sequence, context split). The split's cache rows stream
+// One work-group of W waves (8 for MLRA-4 and most single-latent shapes, 4 for the 16-head
+// MLA shard) owns one (sequence, context split). The split's cache rows stream
 // HBM -> LDS once, through a ring of as many stages as fit in LDS (at most eight) filled by
 // asynchronous LDS-DMA loads, and every query head
 // reads them from LDS: all heads share one cached latent (MLRA page
@@ -27,8 +27,9 @@
 //           the P.C product uses;
 //   values  O^T[feat x head] += C_b^T[feat x tok] . P^T[tok x head], MFMA, with the
 //           transposed latent read by ds_read_b64_tr_b16.
-// With one branch per wave, the score MFMAs of the next sub-tile are issued before the
-// softmax of the current one.
+// The loop is software-pipelined: the score MFMAs of the next sub-tile go out before the
+// softmax of the current one (with several branches per wave, together with the P.C MFMAs of
+// the previous sub-tile, interleaved with the softmax's vector instructions).
 // Each split writes its unnormalised (o, m, l); the merge kernel combines the splits
 // (log-sum-exp) and applies W^V per branch.
 #include <hip/hip_runtime.h>
@@ -46,6 +47,7 @@ typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
 typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
 typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f32x2;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4;
 typedef __attribute__((address_space(3))) char lds_char;
 typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
@@ -53,6 +55,7 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef __attribute__((address_space(3))) const int lds_cint;
 
 constexpr int kMaxStages = 8;
+constexpr int kMfmaGap = 6;                // vector instructions between two matrix instructions of a pipelined block
 constexpr int kSubPerStage = 4;            // 32-token sub-tiles per stage (more when there are more phases)
 constexpr int kLdsBytes = 160 * 1024;
 constexpr int kPageCache = 256;            // page ids of one split kept in LDS (paged mode)
@@ -74,6 +77,11 @@ struct Cfg {
   // one branch per wave: the next sub-tile's scores are issued before the current softmax;
   // with several branches per wave their score tiles leave no registers for that
   static constexpr bool PIPE = BPW == 1;
+  // several branches per wave with two waves per SIMD: the registers hold two sub-tiles'
+  // scores, so the scores of sub-tile k + 1 and the P.C of sub-tile k - 1 are issued in
+  // the same block as the softmax of sub-tile k. The delayed P.C keeps a stage's ring slot
+  // in use until two barriers later, which needs a ring of four stages (the paged instance,
+  // whose page ids leave room for three, runs the same work split unpipelined).
   static constexpr int ST = 32 * SUB;                    // tokens per stage
   static constexpr int NCL = NB * DB / 8;                // latent 16-byte chunks per row
   static constexpr int NCR = DR / 8;                     // RoPE 16-byte chunks per row
@@ -98,6 +106,7 @@ struct Cfg {
   static constexpr int NS_FIT = (kLdsBytes - PTAB_BYTES) / STAGE_BYTES;
   static constexpr int NS = NS_FIT < kMaxStages ? NS_FIT : kMaxStages;   // ring depth
   static constexpr int RING_BYTES = NS * STAGE_BYTES;
+  static constexpr bool PIPE2 = BPW > 1 && W <= 8 && NS >= 4;
   static constexpr int MERGE_BYTES = MERGE_WAVES * MERGE_FLOATS * 4;
   static constexpr int LDS_BYTES = (RING_BYTES > MERGE_BYTES ? RING_BYTES : MERGE_BYTES) + PTAB_BYTES;
   static_assert(NB % BPW == 0, "branches per wave must divide the branches");
@@ -416,7 +425,7 @@ __global__ __launch_bounds__(W * 64, 1) void attn_mfma_kernel(AttnParams p) {
       lsum[h][bb] = 0.f;
       started[h][bb] = false;
     }
-  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+  const s16x4 ones4 = {0x3f80, 0x3f80, 0x3f80, 0x3f80};
 
   // ---- per-sub-tile building blocks ------------------------------------------------------
   // Scores of one 32-token sub-tile for every head group and branch of this wave (raw
@@ -478,15 +487,24 @@ __global__ __launch_bounds__(W * 64, 1) void attn_mfma_kernel(AttnParams p) {
     }
   };
   // p = 2^(x - m) packed to bf16; returns ls + the sum of the packed weights
+  // p = 2^(x - m) packed to bf16; returns ls + the sum of the packed weights. The sum runs on
+  // the matrix pipe, which has room to spare, instead of the vector ALUs, which bound the loop:
+  // a 4x4x4 MFMA whose A operand is all ones leaves in each lane the sum of the four bf16
+  // weights that lane holds in its B operand, so the normaliser sums exactly the weights the
+  // P.C product uses.
   auto weights = [&](int h, int bb, const f32x16& x, bf16x2 (&pk)[8], float ls) __attribute__((always_inline)) -> float {
     const float negm = -mref[h][bb];
+    f32x4 d = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
       f32x2 e = {__builtin_amdgcn_exp2f(fmaf(x[2 * k], qs, negm)), __builtin_amdgcn_exp2f(fmaf(x[2 * k + 1], qs, negm))};
       pk[k] = __builtin_convertvector(e, bf16x2);
-      ls = __builtin_amdgcn_fdot2_f32_bf16(pk[k], ones, ls, false);
+      if (k & 1) {
+        const s16x4 b = __builtin_bit_cast(s16x4, bf16x4{pk[k - 1][0], pk[k - 1][1], pk[k][0], pk[k][1]});
+        d = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(ones4, b, d, 0, 0, 0);
+      }
     }
-    return ls;
+    return ls + d[0];
   };
   // O += P.C for one sub-tile and branch, reading the transposed latent one 32-feature tile at a time
   auto pv_lds = [&](int h, int bb, const bf16x2 (&pk)[8], const lds_char* sub) __attribute__((always_inline)) {
@@ -580,7 +598,7 @@ __global__ __launch_bounds__(W * 64, 1) void attn_mfma_kernel(AttnParams p) {
   // s - 1 when it passes stage s's barrier, so any slot but stage s's may be refilled; two
   // stages ahead measured best there (three ahead was slower on a 4-stage ring, one ahead
   // much slower on the 3-stage ring of the paged instance).
-  constexpr int LOOK = C::PIPE ? C::NS - 2 : 2;
+  constexpr int LOOK = (C::PIPE || C::PIPE2) ? C::NS - 2 : 2;
   for (int s = 0; s < LOOK && s < nst; ++s) issue_stage(s);
   auto begin_piped = [&](int s) __attribute__((always_inline)) {
     const int ahead = min(nst - 1 - s, LOOK - 1);
@@ -626,7 +644,112 @@ __global__ __launch_bounds__(W * 64, 1) void attn_mfma_kernel(AttnParams p) {
       }
   };
   if (K > 0) {
-    if constexpr (C::PIPE) {
+    if constexpr (C::PIPE2) {
+      // softmax of every (head group, branch) of sub-tile k; one vote decides whether any
+      // lane's weights summed past the threshold (then the reference moves and the weights
+      // of that unit are recomputed)
+      // weights of every (head group, branch) of sub-tile k; true if any lane's weights
+      // summed past the threshold
+      auto soft_weights = [&](f32x16 (&cur)[C::HPW][BPW], bf16x2 (&pk)[C::HPW][BPW][8],
+                              float (&ls)[C::HPW][BPW]) __attribute__((always_inline)) -> bool {
+        bool over = false;
+#pragma unroll
+        for (int h = 0; h < C::HPW; ++h)
+#pragma unroll
+          for (int bb = 0; bb < BPW; ++bb) {
+            ls[h][bb] = weights(h, bb, cur[h][bb], pk[h][bb], 0.f);
+            over |= !(ls[h][bb] <= kStageSumMax);
+          }
+        return over;
+      };
+      // one vote decides whether any unit needs the rare path: its reference moves to the
+      // exact max and its weights are recomputed
+      auto soft_finish = [&](bool over, f32x16 (&cur)[C::HPW][BPW], bf16x2 (&pk)[C::HPW][BPW][8],
+                             float (&ls)[C::HPW][BPW]) __attribute__((always_inline)) {
+        if (__builtin_amdgcn_ballot_w64(over) != 0) {
+#pragma unroll
+          for (int h = 0; h < C::HPW; ++h)
+#pragma unroll
+            for (int bb = 0; bb < BPW; ++bb) {
+              if (__builtin_amdgcn_ballot_w64(!(ls[h][bb] <= kStageSumMax)) != 0) {
+                float mx = cur[h][bb][0];
+#pragma unroll
+                for (int r = 1; r < 16; ++r) mx = fmaxf(mx, cur[h][bb][r]);
+                maybe_rescale(h, bb, mx);
+                ls[h][bb] = weights(h, bb, cur[h][bb], pk[h][bb], 0.f);
+              }
+            }
+        }
+#pragma unroll
+        for (int h = 0; h < C::HPW; ++h)
+#pragma unroll
+          for (int bb = 0; bb < BPW; ++bb) lsum[h][bb] += ls[h][bb];
+      };
+      auto soft = [&](f32x16 (&cur)[C::HPW][BPW], bf16x2 (&pk)[C::HPW][BPW][8]) __attribute__((always_inline)) {
+        float ls[C::HPW][BPW];
+        soft_finish(soft_weights(cur, pk, ls), cur, pk, ls);
+      };
+      auto pv_all = [&](int k, const bf16x2 (&pk)[C::HPW][BPW][8]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int h = 0; h < C::HPW; ++h)
+#pragma unroll
+          for (int bb = 0; bb < BPW; ++bb) pv_lds(h, bb, pk[h][bb], sub_of(k));
+      };
+      // Sub-tile k: the scores of k + 1 (NXT) and the P.C of k - 1 (PREV, weights in pkp) go
+      // out with the softmax of k, in one block that the scheduler interleaves, so the
+      // matrix cores work while the vector ALUs do. The P.C of k - 1 precedes any rescale
+      // made by the softmax of k, which therefore scales it with the rest of the
+      // accumulator. BOUNDARY: sub-tile k + 1 opens a stage (wait, barrier, refill first).
+      auto step2 = [&](auto nxt_c, auto prev_c, auto boundary_c, int k, f32x16 (&cur)[C::HPW][BPW],
+                       f32x16 (&nxt)[C::HPW][BPW], bf16x2 (&pkc)[C::HPW][BPW][8],
+                       bf16x2 (&pkp)[C::HPW][BPW][8]) __attribute__((always_inline)) {
+        constexpr bool NXT = decltype(nxt_c)::value, PREV = decltype(prev_c)::value;
+        if constexpr (NXT && decltype(boundary_c)::value) begin_piped((k + 1) / C::NSW);
+        if constexpr (NXT) scores(sub_of(k + 1), nxt);
+        if constexpr (PREV) pv_all(k - 1, pkp);
+        float ls[C::HPW][BPW];
+        const bool over = soft_weights(cur, pkc, ls);
+        if constexpr (NXT || PREV) {
+          // operand reads first, then one matrix instruction per MFMA_GAP vector instructions
+          constexpr int NM = (NXT ? C::HPW * (C::KR + BPW * C::KL) : 0) + (PREV ? C::HPW * BPW * 2 * C::MT : 0);
+          constexpr int ND = (NXT ? C::KR + BPW * C::KL : 0) + (PREV ? C::HPW * BPW * 2 * C::MT * 2 : 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, ND, 0);
+#pragma unroll
+          for (int i = 0; i < NM; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, kMfmaGap, 0);
+          }
+        }
+        soft_finish(over, cur, pkc, ls);
+      };
+      using T_ = std::true_type;
+      using F_ = std::false_type;
+      static_assert(C::NSW == 2, "the unrolled loop puts a stage boundary after every odd sub-tile");
+      begin_piped(0);
+      f32x16 sa[C::HPW][BPW], sb[C::HPW][BPW];
+      bf16x2 pa[C::HPW][BPW][8], pb[C::HPW][BPW][8];
+      scores(sub_of(0), sa);
+      seed(sa);
+      if (K == 1) {
+        soft(sa, pa);
+        pv_all(0, pa);
+      } else {
+        step2(T_{}, F_{}, F_{}, 0, sa, sb, pa, pb);          // k = 0: scores of 1, softmax of 0
+        int k = 1;
+        for (; k + 2 < K; k += 2) {                          // k odd: sub-tile k + 1 opens a stage
+          step2(T_{}, T_{}, T_{}, k, sb, sa, pb, pa);
+          step2(T_{}, T_{}, F_{}, k + 1, sa, sb, pa, pb);
+        }
+        if (K - k == 2) {
+          step2(T_{}, T_{}, T_{}, k, sb, sa, pb, pa);
+          step2(F_{}, T_{}, F_{}, k + 1, sa, sb, pa, pb);
+          pv_all(k + 1, pa);
+        } else {
+          step2(F_{}, T_{}, F_{}, k, sb, sa, pb, pa);
+          pv_all(k, pb);
+        }
+      }
+    } else if constexpr (C::PIPE) {
       // consume the scores `cur` of sub-tile k; first issue the scores of sub-tile k + 1 into `nxt`
       auto step = [&](int k, f32x16 (&cur)[C::HPW][BPW], f32x16 (&nxt)[C::HPW][BPW]) __attribute__((always_inline)) {
         if (k + 1 < K) {
@@ -800,7 +923,7 @@ hipError_t launch_shape(const AttnParams& p, bool paged, int grid_splits, hipStr
 // instances of a shape split the work identically, so they sum every split's tokens in the
 // same order and agree bit for bit.
 #define MLRA_MFMA_SHAPES(X)     \
-  X(4, 32, 32, 64, 16, 2)       \
+  X(4, 32, 32, 64, 8, 2)        \
   X(1, 128, 32, 64, 8, 1)       \
   X(1, 128, 32, 16, 4, 1)       \
   X(1, 32, 32, 16, 8, 1)        \
