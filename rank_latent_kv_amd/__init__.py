@@ -32,8 +32,13 @@ EXPORTED_SYMBOLS = (
     "mlra_last_error", "mlra_version", "mlra_decode_workspace_size", "mlra_decode_validate", "mlra_decode",
     "mla_decode", "mlra_paged_append", "mlra_paged_gather", "mlra_page_table_check", "mlra_page_pool_create",
     "mlra_page_pool_alloc", "mlra_page_pool_free", "mlra_page_pool_num_free", "mlra_page_pool_destroy",
-    "mlra_decode_prepare", "mlra_read_probe_words", "mlra_read_probe",
+    "mlra_decode_prepare", "mlra_read_probe_words", "mlra_read_probe", "mlra_decode_plan",
 )
+MLRA_KERNEL_MFMA = 0
+MLRA_KERNEL_GENERIC = 1
+PLAN_GENERIC_DTYPE = 1
+PLAN_GENERIC_SHAPE = 2
+PLAN_GENERIC_ALIGNMENT = 4
 
 
 class MlraError(RuntimeError):
@@ -58,6 +63,15 @@ class DecodeArgs(ctypes.Structure):
         ("w_v", ctypes.c_void_p), ("out", ctypes.c_void_p), ("workspace", ctypes.c_void_p),
         ("workspace_bytes", ctypes.c_size_t), ("error_flags", ctypes.c_void_p),
         ("event_attn_begin", ctypes.c_void_p), ("event_attn_end", ctypes.c_void_p),
+    ]
+
+
+class PlanInfo(ctypes.Structure):
+    """Mirror of ``mlra_plan_info`` (include/mlra.h)."""
+    _fields_ = [
+        ("kernel", ctypes.c_int32), ("generic_reason", ctypes.c_int32), ("num_splits", ctypes.c_int32),
+        ("split_tokens", ctypes.c_int32), ("work_groups", ctypes.c_int32), ("cu_count", ctypes.c_int32),
+        ("workspace_bytes", ctypes.c_size_t),
     ]
 
 
@@ -111,9 +125,10 @@ def lib() -> ctypes.CDLL:
         L.mlra_read_probe_words.argtypes = []
         L.mlra_read_probe_words.restype = i32
         L.mlra_read_probe.argtypes = [vp, ctypes.c_size_t, vp, i32, vp]
+        L.mlra_decode_plan.argtypes = [P(DecodeArgs), i32, P(PlanInfo)]
         for name in ("mlra_decode_validate", "mlra_decode", "mla_decode", "mlra_decode_prepare", "mlra_paged_append",
                      "mlra_paged_gather", "mlra_page_table_check", "mlra_page_pool_create",
-                     "mlra_page_pool_alloc", "mlra_page_pool_free", "mlra_read_probe"):
+                     "mlra_page_pool_alloc", "mlra_page_pool_free", "mlra_read_probe", "mlra_decode_plan"):
             getattr(L, name).restype = i32
         _lib = L
     return _lib
@@ -140,6 +155,36 @@ def _ptr(t: Optional[torch.Tensor]):
     return None if t is None else t.data_ptr()
 
 
+def _need(t: Optional[torch.Tensor], name: str, *, device: torch.device, dtype=None, contiguous: bool = True,
+          rows_contiguous: bool = False, numel_at_least: Optional[int] = None) -> None:
+    """Refuse a tensor whose raw pointer the library would misread: wrong dtype (an int64 length
+    array read as int32 halves, say), another device, or a layout the C side does not assume.
+    Raises TypeError or ValueError; None passes (optional arguments)."""
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor (got {type(t).__name__})")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, the other operands on {device}")
+    if dtype is not None and t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if contiguous and not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if rows_contiguous and t.dim() > 0 and t.stride(-1) != 1:
+        raise ValueError(f"{name} must have unit stride in its last dimension (got {t.stride(-1)})")
+    if numel_at_least is not None and t.numel() < numel_at_least:
+        raise ValueError(f"{name} holds {t.numel()} elements, needs at least {numel_at_least}")
+
+
+def _need_host_int32(t: Optional[torch.Tensor], name: str, n: int) -> None:
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor) or t.device.type != "cpu" or t.dtype != torch.int32 or not t.is_contiguous():
+        raise TypeError(f"{name} must be a contiguous int32 CPU tensor")
+    if t.numel() < n:
+        raise ValueError(f"{name} holds {t.numel()} entries, needs {n}")
+
+
 def _stream_handle(stream) -> Optional[int]:
     if stream is None:
         return torch.cuda.current_stream().cuda_stream
@@ -159,8 +204,32 @@ def make_args(q_lat, q_rope, kv_lat, kv_rope, seq_lens, w_v, *, sm_scale: float,
     tensor; ``row_stride`` / ``seq_stride`` default to that tensor's strides. The struct
     holds raw pointers, so it keeps a reference to every tensor it points into: the
     memory stays valid for as long as the struct is alive."""
+    if q_lat.dim() != 4:
+        raise ValueError(f"q_lat must be [B, h, n_b, d_b] (got shape {tuple(q_lat.shape)})")
     B, H, NB, DB = q_lat.shape
     DR = q_rope.shape[-1]
+    dev, dt = q_lat.device, q_lat.dtype
+    _dtype_code(dt)
+    _need(q_lat, "q_lat", device=dev)
+    _need(q_rope, "q_rope", device=dev, dtype=dt)
+    if tuple(q_rope.shape) != (B, H, DR):
+        raise ValueError(f"q_rope must be [B, h, d_R] = {(B, H, DR)} (got {tuple(q_rope.shape)})")
+    _need(kv_lat, "kv_lat", device=dev, dtype=dt, contiguous=False, rows_contiguous=True)
+    _need(kv_rope, "kv_rope", device=dev, dtype=dt, contiguous=False, rows_contiguous=True)
+    _need(seq_lens, "seq_lens", device=dev, dtype=torch.int32, numel_at_least=B)
+    _need_host_int32(seq_lens_host, "seq_lens_host", B)
+    _need(page_table, "page_table", device=dev, dtype=torch.int32)
+    if page_table is not None and (page_table.dim() != 2 or page_table.shape[0] < B):
+        raise ValueError(f"page_table must be [B, max_pages] with B >= {B} (got {tuple(page_table.shape)})")
+    # the merge reads W^V in the inputs' dtype
+    _need(w_v, "w_v", device=dev, dtype=dt)
+    if w_v.dim() != 3 or w_v.shape[0] != H or w_v.shape[2] != NB * DB:
+        raise ValueError(f"w_v must be [h, d_h, n_b*d_b] = [{H}, d_h, {NB * DB}] (got {tuple(w_v.shape)})")
+    _need(out, "out", device=dev, dtype=(torch.bfloat16, torch.float32))
+    if out is not None and tuple(out.shape) != (B, H, w_v.shape[1]):
+        raise ValueError(f"out must be [B, h, d_h] = {(B, H, w_v.shape[1])} (got {tuple(out.shape)})")
+    _need(workspace, "workspace", device=dev)
+    _need(error_flags, "error_flags", device=dev, dtype=torch.int32, numel_at_least=1)
     a = DecodeArgs()
     a.batch, a.num_heads, a.num_branches, a.branch_dim, a.rope_dim = B, H, NB, DB, DR
     a.head_dim = w_v.shape[1]
@@ -181,7 +250,6 @@ def make_args(q_lat, q_rope, kv_lat, kv_rope, seq_lens, w_v, *, sm_scale: float,
         a.num_pages = num_pages
     a.seq_lens = _ptr(seq_lens)
     if seq_lens_host is not None:
-        assert seq_lens_host.device.type == "cpu" and seq_lens_host.dtype == torch.int32
         a.seq_lens_host = seq_lens_host.data_ptr()
     a.num_splits = num_splits
     a.w_v, a.out = _ptr(w_v), _ptr(out)
@@ -207,6 +275,19 @@ def alloc_workspace(args: DecodeArgs, device) -> torch.Tensor:
     return torch.empty(n, dtype=torch.uint8, device=device)
 
 
+def plan(args: DecodeArgs, cu_count: int = 0) -> dict:
+    """How a decode call with ``args`` would run: which attention kernel ("mfma" or "generic",
+    with the reasons for the generic one), splits, work-groups and workspace bytes, planned for
+    ``cu_count`` compute units (0 = the current device). Raises MlraError on invalid args."""
+    info = PlanInfo()
+    _check(lib().mlra_decode_plan(ctypes.byref(args), int(cu_count), ctypes.byref(info)))
+    reasons = [n for bit, n in ((PLAN_GENERIC_DTYPE, "dtype"), (PLAN_GENERIC_SHAPE, "shape"),
+                                (PLAN_GENERIC_ALIGNMENT, "alignment")) if info.generic_reason & bit]
+    return {"kernel": "mfma" if info.kernel == MLRA_KERNEL_MFMA else "generic", "generic_reasons": reasons,
+            "num_splits": info.num_splits, "split_tokens": info.split_tokens, "work_groups": info.work_groups,
+            "cu_count": info.cu_count, "workspace_bytes": info.workspace_bytes}
+
+
 def validate(args: DecodeArgs) -> int:
     """Host-only argument check; returns the status code (0 = OK)."""
     return lib().mlra_decode_validate(ctypes.byref(args))
@@ -214,6 +295,8 @@ def validate(args: DecodeArgs) -> int:
 
 def _run(fn_name: str, q_lat, q_rope, kv_lat, kv_rope, seq_lens, w_v, *, sm_scale, alpha, out=None,
          out_dtype=None, workspace=None, stream=None, **kw):
+    if not q_lat.is_cuda:
+        raise ValueError("the decode runs on the GPU: pass device tensors (q_lat is on the CPU)")
     B, H, NB, DB = q_lat.shape
     if out is None:
         out = torch.empty((B, H, w_v.shape[1]), dtype=out_dtype or q_lat.dtype, device=q_lat.device)
@@ -255,6 +338,18 @@ def make_prepare_args(q_nope, q_pe, w_uk_t, c_new, k_pe_new, positions, kv_lat, 
     keeps a reference to every tensor it points into."""
     B, H, DH = q_nope.shape
     DC = w_uk_t.shape[1]
+    dev, dt = q_nope.device, q_nope.dtype
+    _dtype_code(dt)
+    _need(q_nope, "q_nope", device=dev)
+    for name, t in (("q_pe", q_pe), ("w_uk_t", w_uk_t), ("c_new", c_new), ("k_pe_new", k_pe_new), ("q_lat", q_lat),
+                    ("q_rope", q_rope)):
+        _need(t, name, device=dev, dtype=dt)
+    _need(kv_lat, "kv_lat", device=dev, dtype=dt, contiguous=False, rows_contiguous=True)
+    _need(kv_rope, "kv_rope", device=dev, dtype=dt, contiguous=False, rows_contiguous=True)
+    _need(positions, "positions", device=dev, dtype=torch.int32, numel_at_least=B)
+    _need_host_int32(positions_host, "positions_host", B)
+    _need(page_table, "page_table", device=dev, dtype=torch.int32)
+    _need(error_flags, "error_flags", device=dev, dtype=torch.int32, numel_at_least=1)
     a = PrepareArgs()
     a.batch, a.num_heads, a.num_branches = B, H, num_branches
     a.branch_dim, a.rope_dim, a.head_dim = DC // num_branches, q_pe.shape[-1], DH
@@ -263,7 +358,6 @@ def make_prepare_args(q_nope, q_pe, w_uk_t, c_new, k_pe_new, positions, kv_lat, 
     a.q_nope, a.q_pe, a.w_uk = _ptr(q_nope), _ptr(q_pe), _ptr(w_uk_t)
     a.c_new, a.k_pe_new, a.positions = _ptr(c_new), _ptr(k_pe_new), _ptr(positions)
     if positions_host is not None:
-        assert positions_host.device.type == "cpu" and positions_host.dtype == torch.int32
         a.positions_host = positions_host.data_ptr()
     a.q_lat, a.q_rope = _ptr(q_lat), _ptr(q_rope)
     a.kv_lat, a.kv_rope = _ptr(kv_lat), _ptr(kv_rope)
@@ -284,6 +378,8 @@ def prepare(q_nope, q_pe, w_uk_t, c_new, k_pe_new, positions, kv_lat, kv_rope, *
             q_lat: Optional[torch.Tensor] = None, q_rope: Optional[torch.Tensor] = None, stream=None, **kw):
     """The step before a decode call: absorbed query, rotated RoPE query, new cache row.
     Returns (q_lat [B, h, n_b, d_b], q_rope [B, h, d_R])."""
+    if not q_nope.is_cuda:
+        raise ValueError("the prepare step runs on the GPU: pass device tensors (q_nope is on the CPU)")
     B, H, _ = q_nope.shape
     DC = w_uk_t.shape[1]
     if q_lat is None:
@@ -303,9 +399,29 @@ def split_rows(kv: torch.Tensor, latent_dim: int):
 
 # ---- paged cache -------------------------------------------------------------------------
 
+def _check_paged_copy(pool, page_table, lens_or_pos, name, error_flags, rows=None, out=None) -> None:
+    if not pool.is_cuda:
+        raise ValueError("paged copies run on the GPU: pass device tensors (pool is on the CPU)")
+    dev = pool.device
+    _dtype_code(pool.dtype)
+    _need(pool, "pool", device=dev, contiguous=False, rows_contiguous=True)
+    _need(page_table, "page_table", device=dev, dtype=torch.int32)
+    if page_table.dim() != 2:
+        raise ValueError(f"page_table must be [B, max_pages] (got {tuple(page_table.shape)})")
+    _need(lens_or_pos, name, device=dev, dtype=torch.int32, numel_at_least=page_table.shape[0])
+    _need(error_flags, "error_flags", device=dev, dtype=torch.int32, numel_at_least=1)
+    if rows is not None:
+        _need(rows, "rows", device=dev, dtype=pool.dtype, contiguous=False, rows_contiguous=True)
+        if rows.dim() != 2 or rows.shape[-1] > pool.shape[-1]:
+            raise ValueError(f"rows must be [B, R] with R <= the pool row ({pool.shape[-1]})")
+    if out is not None:
+        _need(out, "out", device=dev, dtype=pool.dtype)
+
+
 def paged_append(pool: torch.Tensor, page_table: torch.Tensor, positions: torch.Tensor, rows: torch.Tensor, *,
                  page_size: int, error_flags: Optional[torch.Tensor] = None, stream=None):
     """pool [P, page_size, R] (or any [P*page_size, R] view), rows [B, R]."""
+    _check_paged_copy(pool, page_table, positions, "positions", error_flags, rows=rows)
     R = rows.shape[-1]
     num_pages = pool.numel() // (page_size * pool.shape[-1])
     _check(lib().mlra_paged_append(pool.data_ptr(), pool.stride(-2), R, page_size, num_pages, page_table.data_ptr(),
@@ -316,6 +432,7 @@ def paged_append(pool: torch.Tensor, page_table: torch.Tensor, positions: torch.
 def paged_gather(pool: torch.Tensor, page_table: torch.Tensor, seq_lens: torch.Tensor, max_seq_len: int, *,
                  page_size: int, out: Optional[torch.Tensor] = None, error_flags: Optional[torch.Tensor] = None,
                  stream=None) -> torch.Tensor:
+    _check_paged_copy(pool, page_table, seq_lens, "seq_lens", error_flags, out=out)
     R = pool.shape[-1]
     B = page_table.shape[0]
     if out is None:

@@ -509,3 +509,124 @@ def test_arg_structs_keep_their_tensors_alive():
     del a, pa
     gc.collect()
     assert ref() is None and qref() is None
+
+
+# ---- the binding refuses tensors whose raw pointers the library would misread ----------------
+
+def _small_tensors(dtype=torch.bfloat16):
+    B, H, NB, DB, DR, DH, L = 2, 4, 4, 8, 8, 16, 8
+    kv = torch.zeros(B, L, NB * DB + DR, dtype=dtype)
+    return dict(q_lat=torch.zeros(B, H, NB, DB, dtype=dtype), q_rope=torch.zeros(B, H, DR, dtype=dtype),
+                kv_lat=kv[..., :NB * DB], kv_rope=kv[..., NB * DB:], seq_lens=torch.full((B,), L, dtype=torch.int32),
+                w_v=torch.zeros(H, DH, NB * DB, dtype=dtype))
+
+
+def _make(**over):
+    t = _small_tensors()
+    extra = {k: v for k, v in over.items() if k not in t}
+    t.update({k: v for k, v in over.items() if k in t})
+    return R.make_args(t["q_lat"], t["q_rope"], t["kv_lat"], t["kv_rope"], t["seq_lens"], t["w_v"], sm_scale=1.0,
+                       alpha=1.0, **extra)
+
+
+def test_binding_accepts_consistent_tensors():
+    a = _make()
+    assert a.batch == 2 and a.num_branches == 4 and a.dtype == R.MLRA_BF16
+
+
+def test_binding_refuses_int64_lengths():
+    # int64 [777, 1500] read as int32 would be [777, 0]: refused before any call
+    with pytest.raises(TypeError, match="seq_lens"):
+        _make(seq_lens=torch.tensor([777, 1500]))
+    with pytest.raises(TypeError, match="seq_lens_host"):
+        _make(seq_lens_host=torch.tensor([777, 1500]))
+
+
+def test_binding_refuses_transposed_query():
+    q = torch.zeros(2, 4, 8, 4, dtype=torch.bfloat16).transpose(2, 3)   # [B, h, n_b, d_b] view, not contiguous
+    with pytest.raises(ValueError, match="q_lat must be contiguous"):
+        _make(q_lat=q)
+
+
+def test_binding_refuses_mixed_dtypes():
+    with pytest.raises(TypeError, match="w_v"):
+        _make(w_v=torch.zeros(4, 16, 32, dtype=torch.float32))
+    with pytest.raises(TypeError, match="q_rope"):
+        _make(q_rope=torch.zeros(2, 4, 8, dtype=torch.float32))
+    with pytest.raises(TypeError, match="page_table"):
+        _make(page_table=torch.zeros(2, 4, dtype=torch.int64))
+    with pytest.raises(TypeError, match="error_flags"):
+        _make(error_flags=torch.zeros(1, dtype=torch.int64))
+
+
+def test_binding_refuses_bad_shapes():
+    with pytest.raises(ValueError, match="w_v must be"):
+        _make(w_v=torch.zeros(4, 16, 31, dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match="seq_lens holds"):
+        _make(seq_lens=torch.zeros(1, dtype=torch.int32))
+    with pytest.raises(ValueError, match="unit stride"):
+        kv = torch.zeros(2, 8, 40, dtype=torch.bfloat16)
+        _make(kv_lat=kv[..., 0:32:2][..., :16].expand(2, 8, 16))
+
+
+def test_decode_refuses_host_tensors():
+    t = _small_tensors()
+    with pytest.raises(ValueError, match="GPU"):
+        R.decode(t["q_lat"], t["q_rope"], t["kv_lat"], t["kv_rope"], t["seq_lens"], t["w_v"], sm_scale=1.0, alpha=1.0)
+    pool = torch.zeros(4, 64, 40, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU"):
+        R.paged_append(pool, torch.zeros(2, 2, dtype=torch.int32), torch.zeros(2, dtype=torch.int32),
+                       torch.zeros(2, 40, dtype=torch.bfloat16), page_size=64)
+
+
+# ---- planning for the device's topology, and the kernel-choice report ----------------------
+
+def test_plan_reports_the_mfma_path_at_the_headline_shape():
+    lens = np.full(16, 32768, dtype=np.int32)
+    a = base_args(B=16, L=32768)
+    a.seq_lens_host = lens.ctypes.data
+    p = R.plan(a, cu_count=256)
+    assert p["kernel"] == "mfma" and p["generic_reasons"] == []
+    assert p["num_splits"] == 16 and p["work_groups"] == 256 and p["cu_count"] == 256
+    assert p["workspace_bytes"] == R.lib().mlra_decode_workspace_size(ctypes.byref(a))
+    # without a GPU the current-device plan falls back to the largest gfx950 part
+    assert R.plan(a)["cu_count"] in (256, p["cu_count"]) or torch.cuda.is_available()
+
+
+@pytest.mark.parametrize("cus", [32, 64, 128, 200, 256])
+def test_plan_fits_one_group_per_cu_of_a_mocked_device(cus):
+    """A partitioned or smaller device gets fewer, longer splits: the groups that hold tokens fit
+    one per CU, and the workspace the plan needs never exceeds the size the library reports."""
+    rng = np.random.default_rng(cus)
+    lens = rng.integers(1000, 40000, size=12).astype(np.int32)
+    a = base_args(B=12, L=int(lens.max()))
+    a.seq_lens_host = lens.ctypes.data
+    p = R.plan(a, cu_count=cus)
+    assert p["kernel"] == "mfma" and p["cu_count"] == cus
+    assert p["work_groups"] <= cus or p["num_splits"] == 1
+    # the workspace size and the call plan for the current device (here the fallback, 256 CUs)
+    assert R.plan(a)["workspace_bytes"] == R.lib().mlra_decode_workspace_size(ctypes.byref(a)) or torch.cuda.is_available()
+
+
+def test_plan_reports_the_generic_kernel_and_why():
+    a = base_args(dtype=R.MLRA_F32)
+    p = R.plan(a, cu_count=256)
+    assert p["kernel"] == "generic" and p["generic_reasons"] == ["dtype"]
+    a = base_args(H=32)            # 32 heads: no matrix-core build of this shape
+    p = R.plan(a, cu_count=256)
+    assert p["kernel"] == "generic" and p["generic_reasons"] == ["shape"]
+    a = base_args()
+    a.kv_lat += 2                 # misaligned latent rows
+    a.kv_rope += 2
+    p = R.plan(a, cu_count=256)
+    assert p["kernel"] == "generic" and p["generic_reasons"] == ["alignment"]
+    assert p["work_groups"] == p["num_splits"] * 2 * 64   # one group per (split, sequence, head)
+
+
+def test_plan_rejects_bad_arguments():
+    a = base_args()
+    info = R.PlanInfo()
+    assert R.lib().mlra_decode_plan(ctypes.byref(a), -1, ctypes.byref(info)) == R.MLRA_ERR_INVALID_ARG
+    assert R.lib().mlra_decode_plan(ctypes.byref(a), 256, None) == R.MLRA_ERR_INVALID_ARG
+    a.batch = 0
+    assert R.lib().mlra_decode_plan(ctypes.byref(a), 256, ctypes.byref(info)) == R.MLRA_ERR_INVALID_ARG
