@@ -145,17 +145,49 @@ const char* mlra_last_error(void);
 const char* mlra_version(void);
 
 /*
- * Bytes of workspace a decode call with these arguments needs (pure host
- * function, no HIP call). Returns 0 and sets the error message when the
- * arguments are invalid.
+ * Bytes of workspace a decode call with these arguments needs on the current
+ * device. Host function: it launches nothing; the first call on a device reads
+ * that device's compute-unit and XCD counts (hipDeviceGetAttribute) and keeps
+ * them, exactly as mlra_decode does, so both plan the same splits; without a
+ * usable device it plans for the largest gfx950 part (256 compute units).
+ * Returns 0 and sets the error message when the arguments are invalid.
  */
 size_t mlra_decode_workspace_size(const mlra_decode_args* args);
 
 /*
- * Validate the arguments without launching anything (pure host function).
- * Returns MLRA_OK or the error mlra_decode would return before enqueuing.
+ * Validate the arguments without launching anything (host function; plans for
+ * the current device as mlra_decode_workspace_size does). Returns MLRA_OK or the
+ * error mlra_decode would return before enqueuing.
  */
 mlra_status mlra_decode_validate(const mlra_decode_args* args);
+
+/*
+ * How a decode call with these arguments would run (pointers are checked only
+ * for alignment, since alignment picks the kernel).
+ *   cu_count > 0: plan for a device with that many compute units (a what-if
+ *     query; pure host function, no HIP call);
+ *   cu_count == 0: plan for the current device, whose CU and XCD counts are read
+ *     once with hipDeviceGetAttribute and cached (mlra_decode plans the same way).
+ * kernel tells which attention kernel runs. MLRA_KERNEL_GENERIC (the scalar
+ * kernel: fp32 inputs, shapes without a matrix-core build, misaligned operands,
+ * see generic_reason) runs one work-group per (split, sequence, head) and so
+ * reads the cache once per head, about num_heads times the bytes of the MFMA
+ * path.
+ */
+enum { MLRA_KERNEL_MFMA = 0, MLRA_KERNEL_GENERIC = 1 };
+#define MLRA_PLAN_GENERIC_DTYPE     1u   /* dtype is MLRA_F32 */
+#define MLRA_PLAN_GENERIC_SHAPE     2u   /* no matrix-core build for (n_b, d_b, d_R, h) */
+#define MLRA_PLAN_GENERIC_ALIGNMENT 4u   /* an operand or stride breaks the 16-byte alignment */
+typedef struct mlra_plan_info {
+  int32_t kernel;          /* MLRA_KERNEL_MFMA or MLRA_KERNEL_GENERIC */
+  int32_t generic_reason;  /* MLRA_PLAN_GENERIC_* bits, 0 on the MFMA path */
+  int32_t num_splits;      /* context splits of the longest sequence */
+  int32_t split_tokens;    /* tokens per split */
+  int32_t work_groups;     /* attention work-groups that hold tokens */
+  int32_t cu_count;        /* compute units planned for */
+  size_t workspace_bytes;  /* workspace this plan uses (with cu_count == 0: mlra_decode_workspace_size) */
+} mlra_plan_info;
+mlra_status mlra_decode_plan(const mlra_decode_args* args, int32_t cu_count, mlra_plan_info* info);
 
 /*
  * MLRA decode ([MLRA] §三 and §3.1): per (head, branch) attention over that

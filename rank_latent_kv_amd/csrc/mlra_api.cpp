@@ -1,6 +1,8 @@
 // Host side of libmlra.so: argument validation (no HIP calls), launch planning,
 // the page allocator, and the exported C ABI declared in include/mlra.h.
 #include <algorithm>
+#include <atomic>
+#include <climits>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -42,13 +44,26 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-// Work-groups the automatic split count aims for: one per compute unit of an
-// MI355X: 256 CUs, and the MFMA kernel keeps one work-group per CU.
-constexpr int64_t kTargetGroups = 256;
+// The automatic split count aims for one work-group per compute unit (the MFMA kernel keeps
+// one work-group per CU). The planner takes the device's CU and XCD counts as a parameter,
+// so it stays free of HIP calls. The entry points that plan a real call (decode, workspace
+// size, validation) read the counts of the current device once and keep them; without a
+// usable device they plan for the largest gfx950 part, an MI355X with 256 CUs in 8 XCDs.
+// (The splits are not monotone in the CU count: the shader-engine check below can grow the
+// split on a larger device. So the workspace is sized for the device the call runs on, not
+// for a bound over devices.)
+struct Topology {
+  int cus = 256;
+  int xcds = 8;
+};
+constexpr Topology kLargestGfx950{};
 constexpr int kMaxSplits = 4096;
 constexpr int kPageCache = 256;
 
 struct Plan {
+  int generic_reason = 0;   // MLRA_PLAN_* bits: why the generic kernel runs (0 on the MFMA path)
+  int64_t groups = 0;       // attention work-groups that hold tokens
+  int cus = 0;
   bool mfma = false;
   bool paged = false;
   int stage = 0;          // split granularity in tokens
@@ -68,8 +83,8 @@ int64_t total_tokens_estimate(const mlra_decode_args* a) {
   return (int64_t)a->batch * a->max_seq_len;
 }
 
-// Work-groups of a launch with `split`-token splits (groups past a sequence's end exit
-// at once and are not counted).
+// Work-groups of a launch with `split`-token splits that hold tokens (groups past a
+// sequence's end exit at once).
 int64_t count_groups(const mlra_decode_args* a, int64_t split) {
   if (!a->seq_lens_host) return (int64_t)a->batch * cdiv(a->max_seq_len, split);
   int64_t g = 0;
@@ -77,34 +92,39 @@ int64_t count_groups(const mlra_decode_args* a, int64_t split) {
   return g;
 }
 
-// The MFMA kernel's (splits, batch) grid as MI355X places it: work-groups go to the 8 XCDs
-// in turn (linear id mod 8), and within an XCD to its 4 shader engines in turn, each engine
-// with 8 CUs that hold one group apiece. An engine given a ninth group that holds tokens runs
-// it as a second pass (about twice the kernel time), however many groups of its XCD or of the
-// whole launch are free; groups past a sequence's end exit at once and do not count. This
-// placement matches every launch measured on ragged lengths: those with at most 8 working
-// groups per engine ran in one pass, those with 9 in two. True when no engine gets a ninth.
-constexpr int kXcds = 8;
+// The MFMA kernel's (splits, batch) grid as gfx950 places it: work-groups go to the XCDs in
+// turn (linear id mod XCDs), and within an XCD to its 4 shader engines in turn, each engine
+// with (CUs per XCD) / 4 CUs that hold one group apiece (8 on an MI355X). An engine given
+// one more group than it has CUs runs it as a second pass (about twice the kernel time),
+// however many groups of its XCD or of the whole launch are free; groups past a sequence's
+// end exit at once and do not count. This placement matches every launch measured on ragged
+// lengths of an MI355X: those with at most 8 working groups per engine ran in one pass,
+// those with 9 in two. True when no engine gets more groups than CUs. A device whose CUs do
+// not split evenly over 4 engines per XCD gets only the total-count check.
 constexpr int kEnginesPerXcd = 4;
-bool one_pass_per_engine(const mlra_decode_args* a, int64_t split) {
+constexpr int kMaxEngines = 64;
+bool one_pass_per_engine(const mlra_decode_args* a, int64_t split, const Topology& t) {
   if (!a->seq_lens_host) return true;   // without host lengths the group count alone decides
-  constexpr int kEngines = kXcds * kEnginesPerXcd;
+  if (t.xcds < 1 || t.cus % (t.xcds * kEnginesPerXcd) != 0 || t.xcds * kEnginesPerXcd > kMaxEngines) return true;
+  const int engines = t.xcds * kEnginesPerXcd;
+  const int64_t per_engine = t.cus / engines;
   const int64_t ns = cdiv(a->max_seq_len, split);
-  int64_t working[kEngines] = {};
+  int64_t working[kMaxEngines] = {};
   for (int b = 0; b < a->batch; ++b) {
     const int64_t L = std::min(std::max(a->seq_lens_host[b], 1), a->max_seq_len);
     for (int64_t s = 0; s * split < L; ++s) {
       const int64_t id = b * ns + s;
-      ++working[(id % kXcds) * kEnginesPerXcd + (id / kXcds) % kEnginesPerXcd];
+      ++working[(id % t.xcds) * kEnginesPerXcd + (id / t.xcds) % kEnginesPerXcd];
     }
   }
-  for (int e = 0; e < kEngines; ++e)
-    if (working[e] > kTargetGroups / kEngines) return false;
+  for (int e = 0; e < engines; ++e)
+    if (working[e] > per_engine) return false;
   return true;
 }
 
-// Validate the arguments and decide the launch. Pure host code: no HIP calls.
-mlra_status make_plan(const mlra_decode_args* a, bool check_pointers, Plan* plan) {
+// Validate the arguments and decide the launch for a device of topology `topo`. Pure host
+// code: no HIP calls.
+mlra_status make_plan(const mlra_decode_args* a, bool check_pointers, const Topology& topo, Plan* plan) {
   if (!a) return fail(MLRA_ERR_INVALID_ARG, "args is NULL");
   if (a->batch < 1) return fail(MLRA_ERR_INVALID_ARG, "batch must be >= 1 (got %d)", a->batch);
   if (a->num_heads < 1) return fail(MLRA_ERR_INVALID_ARG, "num_heads must be >= 1 (got %d)", a->num_heads);
@@ -159,15 +179,23 @@ mlra_status make_plan(const mlra_decode_args* a, bool check_pointers, Plan* plan
   if (!mlra::merge_supported(a->num_branches, a->branch_dim, a->head_dim))
     return fail(MLRA_ERR_UNSUPPORTED, "latent width %lld is beyond the merge kernel's limit", (long long)dc);
 
+  if (topo.cus < 1) return fail(MLRA_ERR_INVALID_ARG, "cu count must be >= 1 (got %d)", topo.cus);
+  const int64_t kTargetGroups = topo.cus;
   Plan p;
   p.paged = paged;
+  p.cus = topo.cus;
   const int st = (a->dtype == MLRA_BF16) ? mlra::mfma_stage_tokens(a->num_branches, a->branch_dim, a->rope_dim, a->num_heads) : 0;
   bool mfma = st > 0;
+  if (a->dtype != MLRA_BF16) p.generic_reason |= MLRA_PLAN_GENERIC_DTYPE;
+  else if (st == 0) p.generic_reason |= MLRA_PLAN_GENERIC_SHAPE;
   if (mfma) {
     // the MFMA path moves 16-byte chunks and reads 8-element query groups
     const bool al = aligned(a->q_lat, 16) && aligned(a->q_rope, 16) && aligned(a->kv_lat, 16) && aligned(a->kv_rope, 16) &&
                     a->row_stride % 8 == 0 && (paged || a->seq_stride % 8 == 0);
-    if (!al) mfma = false;
+    if (!al) {
+      mfma = false;
+      p.generic_reason |= MLRA_PLAN_GENERIC_ALIGNMENT;
+    }
   }
   if (!mfma && !mlra::generic_supported(a->num_branches, a->branch_dim, a->rope_dim))
     return fail(MLRA_ERR_UNSUPPORTED, "no kernel for num_branches=%d branch_dim=%d rope_dim=%d dtype=%d", a->num_branches,
@@ -204,7 +232,7 @@ mlra_status make_plan(const mlra_decode_args* a, bool check_pointers, Plan* plan
       }
       split = lo * p.stage;
     }
-    while (split < a->max_seq_len && (count_groups(a, split) > kTargetGroups || !one_pass_per_engine(a, split)))
+    while (split < a->max_seq_len && (count_groups(a, split) > kTargetGroups || !one_pass_per_engine(a, split, topo)))
       split += p.stage;
   }
   if (paged && mfma) {
@@ -219,6 +247,7 @@ mlra_status make_plan(const mlra_decode_args* a, bool check_pointers, Plan* plan
   }
   p.split_tokens = (int)std::min<int64_t>(split, a->max_seq_len + (int64_t)p.stage);
   p.num_splits = (int)cdiv(a->max_seq_len, p.split_tokens);
+  p.groups = count_groups(a, p.split_tokens) * (mfma ? 1 : a->num_heads);
   if (p.num_splits > kMaxSplits)
     return fail(MLRA_ERR_UNSUPPORTED, "%d context splits exceed the limit %d", p.num_splits, kMaxSplits);
   // the vector-ALU merge keeps (m, l) of every split of a block of sequences in LDS
@@ -237,9 +266,45 @@ mlra_status hip_fail(hipError_t e, const char* what) {
   return fail(MLRA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
+// CU and XCD counts of the current device, read once per device and kept for the life of the
+// process (the library's only global state). Without a usable device the largest gfx950 part
+// is assumed.
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_topo_cus[kMaxDevices];
+std::atomic<int> g_topo_xcds[kMaxDevices];
+
+Topology current_topology() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return kLargestGfx950;
+  }
+  Topology t;
+  const int cached = g_topo_cus[dev].load(std::memory_order_acquire);
+  if (cached > 0) {
+    t.cus = cached;
+    t.xcds = g_topo_xcds[dev].load(std::memory_order_relaxed);
+    return t;
+  }
+  int cus = 0, xcds = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) {
+    (void)hipGetLastError();
+    return kLargestGfx950;
+  }
+  if (hipDeviceGetAttribute(&xcds, hipDeviceAttributeNumberOfXccs, dev) != hipSuccess || xcds < 1) {
+    (void)hipGetLastError();
+    xcds = 1;
+  }
+  t.cus = cus;
+  t.xcds = xcds;
+  g_topo_xcds[dev].store(xcds, std::memory_order_relaxed);
+  g_topo_cus[dev].store(cus, std::memory_order_release);
+  return t;
+}
+
 mlra_status run_decode(const mlra_decode_args* a, void* stream_v) {
   Plan plan;
-  mlra_status st = make_plan(a, true, &plan);
+  mlra_status st = make_plan(a, true, current_topology(), &plan);
   if (st != MLRA_OK) return st;
   if (!a->workspace) return fail(MLRA_ERR_WORKSPACE, "workspace is NULL (need %zu bytes)", plan.ws_bytes);
   if (a->workspace_bytes < plan.ws_bytes)
@@ -324,14 +389,38 @@ const char* mlra_version(void) { return "mlra 0.1.0 (gfx950)"; }
 
 size_t mlra_decode_workspace_size(const mlra_decode_args* args) {
   Plan plan;
-  if (make_plan(args, false, &plan) != MLRA_OK) return 0;
+  if (make_plan(args, false, current_topology(), &plan) != MLRA_OK) return 0;
   ok();
   return plan.ws_bytes;
 }
 
+mlra_status mlra_decode_plan(const mlra_decode_args* args, int32_t cu_count, mlra_plan_info* info) {
+  if (!info) return fail(MLRA_ERR_INVALID_ARG, "info is NULL");
+  if (cu_count < 0) return fail(MLRA_ERR_INVALID_ARG, "cu_count must be >= 0 (got %d)", cu_count);
+  Topology t = kLargestGfx950;
+  if (cu_count > 0) {
+    t.cus = cu_count;
+    // XCDs of 32 CUs where the count splits that way, else one
+    t.xcds = cu_count % 32 == 0 ? cu_count / 32 : 1;
+  } else {
+    t = current_topology();
+  }
+  Plan plan;
+  mlra_status st = make_plan(args, false, t, &plan);
+  if (st != MLRA_OK) return st;
+  info->kernel = plan.mfma ? MLRA_KERNEL_MFMA : MLRA_KERNEL_GENERIC;
+  info->generic_reason = plan.generic_reason;
+  info->num_splits = plan.num_splits;
+  info->split_tokens = plan.split_tokens;
+  info->work_groups = (int32_t)std::min<int64_t>(plan.groups, INT32_MAX);
+  info->cu_count = plan.cus;
+  info->workspace_bytes = plan.ws_bytes;
+  return ok();
+}
+
 mlra_status mlra_decode_validate(const mlra_decode_args* args) {
   Plan plan;
-  mlra_status st = make_plan(args, true, &plan);
+  mlra_status st = make_plan(args, true, current_topology(), &plan);
   if (st != MLRA_OK) return st;
   if (!args->workspace) return fail(MLRA_ERR_WORKSPACE, "workspace is NULL (need %zu bytes)", plan.ws_bytes);
   if (args->workspace_bytes < plan.ws_bytes)
