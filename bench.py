@@ -4,15 +4,20 @@
 
 A step is one full decode call of the library, the attention kernel over
 context splits plus the split merge with the W^V epilogue, over one batch of
-synthetic input already resident in HBM. Timed steps rotate among enough
-identical copies of the cache (>= 512 MiB in total) that the 256 MiB Infinity
-Cache cannot serve them. The default warm-up (2000 steps, about 0.1 s at the
-headline) outlasts the GPU's clock ramp under sustained load, so the timed steps
-see its steady state. The one JSON line reports decoded tokens/s (batch /
-step time), the attention kernel's achieved HBM bandwidth (HIP events recorded
-by the library around that kernel, on its stream, on every 16th timed call from
-the 9th, so that the events do not slow the timed calls) against the 8 TB/s peak, and the
-CPU oracle timed on a bounded sample on this host.
+synthetic input already resident in HBM. Steps rotate among enough identical
+copies of the cache (>= 512 MiB in total) that the 256 MiB Infinity Cache cannot
+serve them. W untimed steps, then exactly K steps timed by the wall clock with a
+device synchronisation on both sides give `value` (decoded tokens/s) and
+`ms_per_step`; no timing event sits inside that region.
+
+After it, a separate pass measures the attention kernel alone for the roofline: a
+warm-up of back-to-back calls (so that the kernel is timed in the steady state of a
+long run, not in the first calls after a synchronisation), then calls that alternate
+with and without HIP events recorded by the library around that kernel on its own
+stream. `roofline.achieved` is the kernel's algorithmic bytes over the mean event
+duration; the sample count, median and p10/p90 are reported with it. The CPU oracle
+is timed on a bounded sample on this host (all affinity cores, then one thread), with
+the materialised form on a few (sequence, head) rows reported beside it.
 """
 from __future__ import annotations
 
@@ -73,19 +78,6 @@ def setup(w, inp, dev, copies):
     return d, caches
 
 
-def event_schedule(steps: int, event_every: int):
-    """Which timed calls carry the attention kernel's events: calls k with
-    k % every == phase, n_samples of them, sample j at call phase + j * every.
-
-    The samples sit mid-period (every/2, every/2 + every, ...): the first call after the host
-    synchronisation that opens the timed region starts on an idle GPU and runs 5-25 us slower
-    than the steady calls, a boundary effect of the timing rather than kernel work. Runs too
-    short for that start at call 0."""
-    every = max(1, event_every)
-    phase = every // 2 if steps > every // 2 else 0
-    return every, phase, len(range(phase, steps, every))
-
-
 def make_step_args(w, d, cache, out, ws, lens_host, events=None):
     dc = w.latent_dim
     kv_lat, kv_rope = cache[..., :dc], cache[..., dc:]
@@ -96,44 +88,96 @@ def make_step_args(w, d, cache, out, ws, lens_host, events=None):
     return R.make_args(d["q_lat"], d["q_rope"], kv_lat, kv_rope, d["seq_lens"], d["w_v"], **kw)
 
 
-def cpu_baseline(w, inp, budget_s: float):
-    """The CPU oracle as it stands, on whole sequences of the batch, pass after
-    pass, until the time budget is spent (at least one sequence). Returns
-    (tokens/s, sequences done, seconds, threads, y of the first pass)."""
+def _oracle_rows(w, inp, beta):
+    """Sequence beta's cached rows as fp64 [1, L, row] (gathered through the page table when paged)."""
+    L = int(inp["seq_lens"][beta])
+    if w.paged:
+        pool = inp["pool"]
+        n = -(-L // w.page_size)
+        ids = torch.from_numpy(inp["page_table"].numpy()[beta, :n]).long()
+        rows = pool[ids].reshape(1, -1, pool.shape[-1])[:, :L]
+    else:
+        rows = inp["kv"][beta:beta + 1, :L]
+    return rows.double().numpy()
+
+
+def _oracle_pass(w, inp, budget_s: float, max_seqs: int = 10 ** 6):
+    """Whole sequences of the batch through the absorbed-form oracle, pass after pass, until
+    the budget is spent (at least one). Returns (sequences, seconds, y of the first pass)."""
     from oracle import mlra_oracle as O
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
-    except Exception:
-        threads = 1
     lens = inp["seq_lens"].numpy()
     dc = w.latent_dim
+    w_v = inp["w_v"].double().numpy()
     done, ys = 0, []
     t0 = time.perf_counter()
-    for step in range(10 ** 6):
+    for step in range(max_seqs):
         beta = step % w.batch
-        q_lat = inp["q_lat"][beta:beta + 1].double().numpy()
-        q_rope = inp["q_rope"][beta:beta + 1].double().numpy()
-        w_v = inp["w_v"].double().numpy()
-        if w.paged:
-            pool = inp["pool"]
-            pt = inp["page_table"].numpy()[beta:beta + 1]
-            n = -(-int(lens[beta]) // w.page_size)
-            rows = pool[torch.from_numpy(pt[0, :n]).long()].reshape(1, -1, pool.shape[-1])[:, :lens[beta]]
-            rows = rows.double().numpy()
-            y = O.mlra_decode_absorbed(q_lat, q_rope, rows[:, :, :dc], rows[:, :, dc:], lens[beta:beta + 1], w_v,
-                                       w.sm_scale, w.alpha)
-        else:
-            kv = inp["kv"][beta:beta + 1, :lens[beta]].double().numpy()
-            y = O.mlra_decode_absorbed(q_lat, q_rope, kv[:, :, :dc], kv[:, :, dc:], lens[beta:beta + 1], w_v,
-                                       w.sm_scale, w.alpha)
+        rows = _oracle_rows(w, inp, beta)
+        y = O.mlra_decode_absorbed(inp["q_lat"][beta:beta + 1].double().numpy(),
+                                   inp["q_rope"][beta:beta + 1].double().numpy(), rows[:, :, :dc], rows[:, :, dc:],
+                                   lens[beta:beta + 1], w_v, w.sm_scale, w.alpha)
         if step < w.batch:
             ys.append(y[0])
         done += 1
         if time.perf_counter() - t0 > budget_s:
             break
-    dt = time.perf_counter() - t0
-    return done / dt, done, dt, threads, np.stack(ys)
+    return done, time.perf_counter() - t0, ys
+
+
+def cpu_baseline(w, inp, budget_s: float):
+    """The CPU oracle as it stands, timed on this host. Returns (cpu_baseline dict, y of the
+    sequences the first pass covered).
+
+    - value: the absorbed-form fp64 oracle over whole sequences, pass after pass for about
+      budget_s, with the BLAS pool allowed every core of this process's affinity set;
+    - single_thread: the same on one thread, over one sequence;
+    - materialised_subset: the materialised form (per-branch keys and values built from the
+      non-absorbed up-projections) on sequence 0 and a seeded set of 4 heads, with its largest
+      relative difference from the absorbed form on those rows."""
+    from threadpoolctl import threadpool_info, threadpool_limits
+    from oracle import mlra_oracle as O
+    cores = len(os.sched_getaffinity(0))
+    with threadpool_limits(limits=cores):
+        blas_threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+        done, dt, ys = _oracle_pass(w, inp, budget_s)
+    with threadpool_limits(limits=1):
+        done1, dt1, _ = _oracle_pass(w, inp, 0.0, max_seqs=1)
+        rng = np.random.Generator(np.random.PCG64(11))
+        heads = sorted(rng.choice(w.heads, size=min(4, w.heads), replace=False).tolist())
+        rows = _oracle_rows(w, inp, 0)
+        q_lat = inp["q_lat"][0:1].double().numpy()
+        q_nope, w_k = O.absorption_consistent_query(q_lat, max(w.head_dim, w.latent_dim), rng)
+        t0 = time.perf_counter()
+        ym = O.mlra_decode_materialised(q_nope, w_k, inp["q_rope"][0:1].double().numpy(), rows[:, :, :w.latent_dim],
+                                        rows[:, :, w.latent_dim:], inp["seq_lens"].numpy()[0:1],
+                                        inp["w_v"].double().numpy(), w.sm_scale, w.alpha, w.branches,
+                                        seqs=[0], heads=heads)
+        dtm = time.perf_counter() - t0
+    ya = ys[0][heads]
+    mat_err = float(np.max(np.abs(ym[0, heads] - ya)) / max(float(np.max(np.abs(ya))), 1e-300))
+    L0 = int(inp["seq_lens"][0])
+    out = {"value": done / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+           "sample": f"{done} whole-context sequences (passes over the {w.batch}-sequence batch), fp64 numpy "
+                     f"absorbed-form oracle, {dt:.1f} s, BLAS threads {blas_threads} of {cores} affinity cores",
+           "blas_threads": blas_threads,
+           "single_thread": {"value": done1 / dt1, "unit": "tokens/s", "seconds": dt1,
+                             "sample": f"{done1} sequence(s) on one thread"},
+           "materialised_subset": {"seconds": dtm, "rows": f"sequence 0 (L={L0}) x heads {heads}",
+                                   "max_rel_diff_vs_absorbed": mat_err}}
+    return out, np.stack(ys)
+
+
+def event_pass(fn, args_list, ev_args, stream, warm: int, samples: int):
+    """Time the attention kernel alone: `warm` back-to-back calls, then 2 * samples calls
+    alternating an event-bracketed call with a plain one. Returns the event durations in us."""
+    import ctypes
+    n = len(args_list)
+    for k in range(warm):
+        fn(ctypes.byref(args_list[k % n]), stream)
+    for j in range(samples):
+        fn(ctypes.byref(ev_args[j]), stream)
+        fn(ctypes.byref(args_list[j % n]), stream)
+    return ev_args
 
 
 def reduce_pmc(workload: str, fetch_csv: str, write_csv: str, command: str) -> str:
@@ -245,8 +289,10 @@ def main():
     ap.add_argument("--seq-len", type=int, default=0, help="override every sequence's length (reported in config)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
-    ap.add_argument("--event-every", type=int, default=16,
-                    help="record the attention kernel's HIP events on every N-th timed call (1 = every call)")
+    ap.add_argument("--event-samples", type=int, default=40,
+                    help="event-bracketed attention-kernel launches in the roofline pass after the timed region")
+    ap.add_argument("--event-warmup", type=int, default=1000,
+                    help="back-to-back calls before the roofline samples, so that they see the steady state")
     ap.add_argument("--prepare", action="store_true",
                     help="time the prepare step (query absorption, RoPE, new cache row) before each decode call")
     ap.add_argument("--calibration-copy", action="store_true",
@@ -302,21 +348,24 @@ def main():
     a0.num_splits = args.num_splits
     ws = torch.empty(R.workspace_size(a0), dtype=torch.uint8, device=dev)
     K, W = args.steps, args.warmup
-    # HIP events around the attention kernel of every event_every-th call: a pair on every call adds
-    # about 5 us to each call's wall time, so the timed calls are sampled evenly instead
-    every, phase, n_samples = event_schedule(K, args.event_every)
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(n_samples)]
-    for e0, e1 in evs:      # materialise the HIP events so the library can record them
-        e0.record()
-        e1.record()
     step_args = []
     for k in range(K):
         c = k % copies
-        ev = (evs[k // every][0].cuda_event, evs[k // every][1].cuda_event) if k % every == phase else None
-        a = make_step_args(w, d, caches[c], outs[c], ws, lens_host, events=ev)
+        a = make_step_args(w, d, caches[c], outs[c], ws, lens_host)
         a.num_splits = args.num_splits
         step_args.append(a)
+    # the roofline pass: HIP events recorded by the library around the attention kernel alone
+    n_ev = max(20, args.event_samples)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_ev)]
+    for e0, e1 in evs:      # materialise the HIP events so the library can record them
+        e0.record()
+        e1.record()
+    ev_args = []
+    for j, (e0, e1) in enumerate(evs):
+        a = make_step_args(w, d, caches[(j + 1) % copies], outs[(j + 1) % copies], ws, lens_host,
+                           events=(e0.cuda_event, e1.cuda_event))
+        a.num_splits = args.num_splits
+        ev_args.append(a)
     warm_args = []
     for k in range(W):
         a = make_step_args(w, d, caches[k % copies], outs[k % copies], ws, lens_host)
@@ -371,6 +420,13 @@ def main():
     if R.last_error():
         raise RuntimeError(R.last_error())
     step_s = (t1 - t0) / K
+    y_last = outs[(K - 1) % copies].float().cpu().double().numpy()
+
+    # roofline pass, after the timed region: its warm-up and events do not touch ms_per_step
+    event_pass(fn, step_args, ev_args, stream, args.event_warmup, n_ev)
+    torch.cuda.synchronize()
+    if R.last_error():
+        raise RuntimeError(R.last_error())
     attn_ms = np.array([e0.elapsed_time(e1) for e0, e1 in evs])
     attn_s = float(np.mean(attn_ms)) * 1e-3
 
@@ -407,19 +463,18 @@ def main():
                      "avg_launch_us": attn_s * 1e6, "median_us": float(np.median(attn_ms)) * 1e3,
                      "p10_us": float(np.percentile(attn_ms, 10)) * 1e3,
                      "p90_us": float(np.percentile(attn_ms, 90)) * 1e3,
-                     "event_samples": len(evs), "event_every": every, "event_first_call": phase,
+                     "event_samples": len(evs), "event_pass": f"after the timed region: {args.event_warmup} "
+                     f"back-to-back calls, then {n_ev} event-bracketed calls each followed by a plain one",
                      "mfma_tflops": af["attention"] / attn_s / 1e12},
     }
 
     # parity of this exact launch configuration against the oracle on the sampled sequences
     if not args.no_cpu_baseline:
-        tps, done, dt, threads, yref = cpu_baseline(w, inp, args.cpu_budget)
-        yg = outs[(K - 1) % copies][:len(yref)].float().cpu().double().numpy()
+        cb, yref = cpu_baseline(w, inp, args.cpu_budget)
+        yg = y_last[:len(yref)]
         num = np.max(np.abs(yg - yref), axis=-1)
         den = np.maximum(np.max(np.abs(yref), axis=-1), 1e-30)
-        result["cpu_baseline"] = {"value": tps, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-                                  "sample": f"{done} whole-context sequences (passes over the {w.batch}-sequence "
-                                            f"batch), fp64 numpy absorbed-form oracle, {dt:.1f} s"}
+        result["cpu_baseline"] = cb
         # with --prepare the decode ran on the prepared queries and cache row, not on these inputs
         result["parity_max_row_rel_err"] = None if args.prepare else float(np.max(num / den))
     print(json.dumps(result), flush=True)
