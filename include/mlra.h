@@ -178,6 +178,7 @@ enum { MLRA_KERNEL_MFMA = 0, MLRA_KERNEL_GENERIC = 1 };
 #define MLRA_PLAN_GENERIC_DTYPE     1u   /* dtype is MLRA_F32 */
 #define MLRA_PLAN_GENERIC_SHAPE     2u   /* no matrix-core build for (n_b, d_b, d_R, h) */
 #define MLRA_PLAN_GENERIC_ALIGNMENT 4u   /* an operand or stride breaks the 16-byte alignment */
+#define MLRA_PLAN_GENERIC_PAGE_SIZE 8u   /* pages smaller than the matrix-core kernel takes (16 tokens for MLRA-4) */
 typedef struct mlra_plan_info {
   int32_t kernel;          /* MLRA_KERNEL_MFMA or MLRA_KERNEL_GENERIC */
   int32_t generic_reason;  /* MLRA_PLAN_GENERIC_* bits, 0 on the MFMA path */

@@ -39,6 +39,7 @@ MLRA_KERNEL_GENERIC = 1
 PLAN_GENERIC_DTYPE = 1
 PLAN_GENERIC_SHAPE = 2
 PLAN_GENERIC_ALIGNMENT = 4
+PLAN_GENERIC_PAGE_SIZE = 8
 
 
 class MlraError(RuntimeError):
@@ -282,7 +283,8 @@ def plan(args: DecodeArgs, cu_count: int = 0) -> dict:
     info = PlanInfo()
     _check(lib().mlra_decode_plan(ctypes.byref(args), int(cu_count), ctypes.byref(info)))
     reasons = [n for bit, n in ((PLAN_GENERIC_DTYPE, "dtype"), (PLAN_GENERIC_SHAPE, "shape"),
-                                (PLAN_GENERIC_ALIGNMENT, "alignment")) if info.generic_reason & bit]
+                                (PLAN_GENERIC_ALIGNMENT, "alignment"), (PLAN_GENERIC_PAGE_SIZE, "page_size"))
+               if info.generic_reason & bit]
     return {"kernel": "mfma" if info.kernel == MLRA_KERNEL_MFMA else "generic", "generic_reasons": reasons,
             "num_splits": info.num_splits, "split_tokens": info.split_tokens, "work_groups": info.work_groups,
             "cu_count": info.cu_count, "workspace_bytes": info.workspace_bytes}

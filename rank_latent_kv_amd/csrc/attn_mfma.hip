@@ -59,6 +59,7 @@ constexpr int kMfmaGap = 6;                // vector instructions between two ma
 constexpr int kSubPerStage = 4;            // 32-token sub-tiles per stage (more when there are more phases)
 constexpr int kLdsBytes = 160 * 1024;
 constexpr int kPageCache = 256;            // page ids of one split kept in LDS (paged mode)
+constexpr int kPageLanes = 64;             // or in one register, one page id per lane
 constexpr float kRescaleThreshold = 8.0f;  // log2 units: p = 2^x stays <= 256
 constexpr float kStageSumMax = 65536.0f;   // a lane's sub-tile weights summing past this trigger the exact max
 
@@ -100,9 +101,18 @@ struct Cfg {
   static constexpr int MT = DB / 32;                     // value M-tiles (32 features)
   static constexpr int KR = DR / 16;                     // RoPE K-chunks of the score
   static constexpr int KL = DB / 16;                     // latent K-chunks of the score
+  static constexpr int QL_BYTES = HEADS * NB * DB * 2;  // one sequence's absorbed queries
+  static constexpr int QR_BYTES = HEADS * DR * 2;       // and RoPE queries
+  static constexpr int QL_DMA = (QL_BYTES + 1023) / 1024;
+  static constexpr int QR_DMA = (QR_BYTES + 1023) / 1024;
   static constexpr int MERGE_WAVES = P > 1 ? W : 0;     // every wave publishes a merge record
   static constexpr int MERGE_FLOATS = HPW * BPW * (16 * MT + 2) * 64;   // per wave record
-  static constexpr int PTAB_BYTES = PAGED ? kPageCache * 4 : 0;
+  // Paged instances with several branches per wave keep the split's page ids in registers and
+  // give each wave a block of TPW consecutive tokens per stage (one page when pages hold at
+  // least TPW tokens), so the ring keeps all of LDS; the others cache the page ids in LDS.
+  static constexpr bool PAGE_REGS = PAGED && BPW > 1;
+  static constexpr int TPW = DMA_HI * 64 / NCH;          // tokens per wave per stage (blocked plan)
+  static constexpr int PTAB_BYTES = (PAGED && !PAGE_REGS) ? kPageCache * 4 : 0;
   static constexpr int NS_FIT = (kLdsBytes - PTAB_BYTES) / STAGE_BYTES;
   static constexpr int NS = NS_FIT < kMaxStages ? NS_FIT : kMaxStages;   // ring depth
   static constexpr int RING_BYTES = NS * STAGE_BYTES;
@@ -117,7 +127,11 @@ struct Cfg {
   static_assert((NCH % 8 == 0 && NCH >= 8) || NCH % 16 == 4, "chunk rotation assumes NCH = 0 mod 8 or 4 mod 16");
   static_assert(NS >= 3, "the ring needs three stages");
   static_assert(DMA_HI * (NS - 2) < 64, "vmcnt range of the DMA waits");
+  static_assert(!PAGE_REGS || (DMA_PER_STAGE == W * DMA_HI && (DMA_HI * 64) % NCH == 0 && ST == W * TPW),
+                "the blocked DMA plan gives every wave the same whole tokens");
   static_assert(LDS_BYTES <= kLdsBytes, "LDS budget");
+  static_assert((QL_DMA + QR_DMA) * 1024 <= STAGE_BYTES, "the queries fit one ring slot");
+  static_assert(QL_BYTES % 16 == 0 && QR_BYTES % 16 == 0, "16-byte query chunks");
 };
 
 // Rotation of the 16-byte chunk positions of token t inside its LDS row. The LDS
@@ -199,9 +213,6 @@ __device__ __forceinline__ float halves_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-__device__ __forceinline__ bf16x8 load_q8(const __bf16* src) {
-  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(src));
-}
 
 template <int NB, int DB, int DR, int HEADS, int W, bool PAGED, int BPW>
 __global__ __launch_bounds__(W * 64, 1) void attn_mfma_kernel(AttnParams p) {
@@ -231,21 +242,34 @@ __global__ __launch_bounds__(W * 64, 1) void attn_mfma_kernel(AttnParams p) {
   const int g = lane >> 5;          // lane half
   const int n32 = lane & 31;        // head within a group / token within a sub-tile
 
-  // ---- paged: this split's page ids into LDS -------------------------------------------
+  // ---- paged: this split's page ids, in LDS or in registers (lane l of register k holds
+  // page first_page + 64 k + l) ---------------------------------------------------------------
   int first_page = 0;
+  int preg = 0;
   if constexpr (PAGED) {
     first_page = t0 >> p.page_shift;
-    const int last_page = (t1 - 1) >> p.page_shift;
-    for (int i = tid; i <= last_page - first_page; i += C::THREADS) {
-      int pg = p.page_table[(int64_t)beta * p.max_pages + first_page + i];
+    const int npages = ((t1 - 1) >> p.page_shift) - first_page + 1;
+    auto checked = [&](int pg) __attribute__((always_inline)) {
       if (pg < 0 || pg >= p.num_pages) {
         if (p.error_flags) atomicOr(p.error_flags, 2u);
         pg = 0;
       }
-      ptab[i] = pg;
+      return pg;
+    };
+    if constexpr (C::PAGE_REGS) {
+      // a split spans at most kPageLanes pages (the host sizes splits so)
+      if (lane < npages) preg = checked(p.page_table[(int64_t)beta * p.max_pages + first_page + lane]);
+    } else {
+      for (int i = tid; i < npages; i += C::THREADS) ptab[i] = checked(p.page_table[(int64_t)beta * p.max_pages + first_page + i]);
+      __syncthreads();
     }
-    __syncthreads();
   }
+  // the page id of the split's page pi (< kPageLanes): the same pi in every lane (one register
+  // read) or one pi per lane (a cross-lane permute)
+  auto page_uniform = [&](int pi) __attribute__((always_inline)) -> int { return __builtin_amdgcn_readlane(preg, pi); };
+  auto page_lane = [&](int pi) __attribute__((always_inline)) -> int {
+    return __builtin_amdgcn_ds_bpermute(pi << 2, preg);
+  };
 
   // ---- DMA lane plan (stage-invariant) --------------------------------------------------
   // wave w < DW issues the stage's DMA instructions w, w + DW, w + 2 DW, ...; the first
@@ -257,8 +281,13 @@ __global__ __launch_bounds__(W * 64, 1) void attn_mfma_kernel(AttnParams p) {
     int tok;
     int chunk;
   };
+  // the stage's DMA instruction that this wave's i-th one is: interleaved over the waves, or
+  // (page ids in registers) blocked, wave w moving tokens [w TPW, (w + 1) TPW) of the stage
+  auto dma_index = [&](int i) __attribute__((always_inline)) -> int {
+    return C::PAGE_REGS ? wave * C::DMA_HI + i : min(wave + C::DW * i, C::DMA_PER_STAGE - 1);
+  };
   auto dma_lane = [&](int i, int ln) __attribute__((always_inline)) -> DmaLane {
-    const int f = min(wave + C::DW * i, C::DMA_PER_STAGE - 1) * 64 + ln;
+    const int f = dma_index(i) * 64 + ln;
     const int t = f / C::NCH;
     int c = f - t * C::NCH - chunk_rot<C::NCH>(t);
     if (c < 0) c += C::NCH;
@@ -285,7 +314,10 @@ __global__ __launch_bounds__(W * 64, 1) void attn_mfma_kernel(AttnParams p) {
   for (int i = 0; i < C::DMA_HI; ++i) {
     const DmaLane d = dma_lane(i, lane);
     const char* sel = chunk_src(d.chunk);
-    if constexpr (PAGED) {
+    if constexpr (C::PAGE_REGS) {
+      dptr[i] = sel + (int64_t)(d.tok - wave * C::TPW) * p.row_stride_b;   // row inside the wave's block
+      pid_addr[i] = 0;
+    } else if constexpr (PAGED) {
       const int rin = big_pages ? d.tok : (d.tok & pmask);
       dptr[i] = sel + (int64_t)rin * p.row_stride_b;
       pid_addr[i] = ptab_lds + 4u * (uint32_t)(big_pages ? 0 : (d.tok >> p.page_shift));
@@ -304,7 +336,16 @@ __global__ __launch_bounds__(W * 64, 1) void attn_mfma_kernel(AttnParams p) {
     if (tok0 + C::ST <= t1) {
       // full stage: one pointer add (and for small pages one LDS page-id read) per DMA
       const uint32_t slot0 = ring + (uint32_t)(wave * 1024);
-      if constexpr (PAGED) {
+      if constexpr (C::PAGE_REGS) {
+        // this wave's TPW tokens lie in one page (pages hold at least TPW tokens, checked on the
+        // host): one uniform page id and one uniform offset for all its DMAs
+        const int tw = tok0 + wave * C::TPW;
+        const int pg = page_uniform((tw >> p.page_shift) - first_page);
+        const int64_t off = (int64_t)((uint64_t)(uint32_t)pg * page_bytes32) + (int64_t)(tw & pmask) * p.row_stride_b;
+#pragma unroll
+        for (int i = 0; i < C::DMA_HI; ++i)
+          dma16(dptr[i] + off, __builtin_amdgcn_readfirstlane(ring + (uint32_t)(dma_index(i) * 1024)));
+      } else if constexpr (PAGED) {
         if (big_pages) {
           // one page holds the whole stage: a uniform offset
           const int pg = __builtin_amdgcn_readfirstlane(ptab[(tok0 >> p.page_shift) - first_page]);
@@ -347,7 +388,11 @@ __global__ __launch_bounds__(W * 64, 1) void attn_mfma_kernel(AttnParams p) {
         const DmaLane d = dma_lane(i, ln);
         const int tok = min(tok0 + d.tok, t1 - 1);
         int64_t row, row_of_dptr;
-        if constexpr (PAGED) {
+        if constexpr (C::PAGE_REGS) {
+          const int pg = page_lane((tok >> p.page_shift) - first_page);
+          row = ((int64_t)pg << p.page_shift) | (tok & pmask);
+          row_of_dptr = d.tok - wave * C::TPW;
+        } else if constexpr (PAGED) {
           const int pg = ptab[(tok >> p.page_shift) - first_page];
           row = ((int64_t)pg << p.page_shift) | (tok & pmask);
           row_of_dptr = big_pages ? d.tok : (d.tok & pmask);
@@ -356,29 +401,48 @@ __global__ __launch_bounds__(W * 64, 1) void attn_mfma_kernel(AttnParams p) {
           row_of_dptr = t0 + d.tok;
         }
         const char* src = dptr[i] + (row - row_of_dptr) * p.row_stride_b;
-        dma16(src, __builtin_amdgcn_readfirstlane(ring + (uint32_t)((wave + C::DW * i) * 1024)));
+        dma16(src, __builtin_amdgcn_readfirstlane(ring + (uint32_t)(dma_index(i) * 1024)));
       }
     }
   };
 
   // ---- queries: B operands (exact bf16 values) ---------------------------------------------
+  // The sequence's queries (q_lat then q_rope, HEADS x (d_c + d_R) bf16) are copied into the
+  // last ring slot by LDS-DMA together with stage 0, and every wave reads its operands from
+  // there right after the first barrier. Through the DMA their arrival is covered by the
+  // kernel's own vmcnt accounting; loaded into registers directly, the compiler would wait for
+  // every outstanding load (the stages in flight included) before the first score MFMA.
   bf16x8 qr[C::HPW][C::KR];
   bf16x8 ql[C::HPW][BPW][C::KL];
+  const uint32_t q_lds = smem_lds + (uint32_t)((C::NS - 1) * C::STAGE_BYTES);
+  auto issue_queries = [&]() __attribute__((always_inline)) {
+    const char* ql_src = reinterpret_cast<const char*>(p.q_lat) + (int64_t)beta * C::QL_BYTES;
+    const char* qr_src = reinterpret_cast<const char*>(p.q_rope) + (int64_t)beta * C::QR_BYTES;
+    for (int i = wave; i < C::QL_DMA; i += C::WAVES)
+      if (i * 64 + lane < C::QL_BYTES / 16)
+        dma16(ql_src + (i * 64 + lane) * 16, __builtin_amdgcn_readfirstlane(q_lds + (uint32_t)(i * 1024)));
+    for (int i = wave; i < C::QR_DMA; i += C::WAVES)
+      if (i * 64 + lane < C::QR_BYTES / 16)
+        dma16(qr_src + (i * 64 + lane) * 16,
+              __builtin_amdgcn_readfirstlane(q_lds + (uint32_t)(C::QL_DMA * 1024 + i * 1024)));
+  };
+  auto read_queries = [&]() __attribute__((always_inline)) {
+    const lds_char* qb = (const lds_char*)smem + (C::NS - 1) * C::STAGE_BYTES;
 #pragma unroll
-  for (int h = 0; h < C::HPW; ++h) {
-    const int head = (hgslot * C::HPW + h) * 32 + n32;
-    const bool live = head < p.H;
-    const __bf16* qrp = reinterpret_cast<const __bf16*>(p.q_rope) + ((int64_t)beta * p.H + head) * DR;
+    for (int h = 0; h < C::HPW; ++h) {
+      const int head = (hgslot * C::HPW + h) * 32 + n32;
+      const bool live = head < HEADS;
 #pragma unroll
-    for (int k = 0; k < C::KR; ++k) qr[h][k] = live ? load_q8(qrp + 16 * k + 8 * g) : bf16x8{};
+      for (int k = 0; k < C::KR; ++k)
+        qr[h][k] = live ? *(const lds_bf16x8*)(qb + C::QL_DMA * 1024 + (head * DR + 16 * k + 8 * g) * 2) : bf16x8{};
 #pragma unroll
-    for (int bb = 0; bb < BPW; ++bb) {
-      const __bf16* qlp =
-          reinterpret_cast<const __bf16*>(p.q_lat) + (((int64_t)beta * p.H + head) * NB + bg * BPW + bb) * DB;
+      for (int bb = 0; bb < BPW; ++bb)
 #pragma unroll
-      for (int k = 0; k < C::KL; ++k) ql[h][bb][k] = live ? load_q8(qlp + 16 * k + 8 * g) : bf16x8{};
+        for (int k = 0; k < C::KL; ++k)
+          ql[h][bb][k] = live ? *(const lds_bf16x8*)(qb + ((head * NB + bg * BPW + bb) * DB + 16 * k + 8 * g) * 2)
+                              : bf16x8{};
     }
-  }
+  };
 
   // ---- per-lane LDS offsets inside a sub-tile -------------------------------------------
   int off_r[C::KR], off_l[BPW][C::KL], off_v[BPW][C::MT][2];
@@ -599,12 +663,24 @@ __global__ __launch_bounds__(W * 64, 1) void attn_mfma_kernel(AttnParams p) {
   // stages ahead measured best there (three ahead was slower on a 4-stage ring, one ahead
   // much slower on the 3-stage ring of the paged instance).
   constexpr int LOOK = (C::PIPE || C::PIPE2) ? C::NS - 2 : 2;
-  for (int s = 0; s < LOOK && s < nst; ++s) issue_stage(s);
+  // stage 0 first, then the queries (into the last ring slot, which the prologue's stages do
+  // not use: LOOK <= NS - 1), then the rest of the prologue's stages
+  static_assert(LOOK <= C::NS - 1, "the prologue leaves the query slot free");
+  issue_stage(0);
+  issue_queries();
+  for (int s = 1; s < LOOK && s < nst; ++s) issue_stage(s);
+  // Wait for stage s (the queries with stage 0: they went out before stage 1), barrier, refill
+  // LOOK stages ahead. At s = 0 the waves first read their query operands from the last ring
+  // slot and wait for those reads, since the refill may target that slot.
   auto begin_piped = [&](int s) __attribute__((always_inline)) {
     const int ahead = min(nst - 1 - s, LOOK - 1);
     if (ndma == C::DMA_HI) wait_dma<C::DMA_HI, LOOK - 1>(ahead);
     else wait_dma<C::DMA_LO, LOOK - 1>(ahead);
     block_barrier();
+    if (s == 0) {
+      read_queries();
+      asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory");
+    }
     if (s + LOOK < nst) issue_stage(s + LOOK);
   };
   auto sub_of = [&](int k) __attribute__((always_inline)) {
@@ -929,6 +1005,26 @@ hipError_t launch_shape(const AttnParams& p, bool paged, int grid_splits, hipStr
   X(1, 32, 32, 16, 8, 1)        \
   X(1, 32, 32, 64, 8, 1)        \
   X(2, 64, 32, 64, 8, 1)
+
+int mfma_page_cache(int nb, int db, int dr, int heads) {
+#define X(xNB, xDB, xDR, xH, xW, xBPW)                                                 \
+  if (nb == xNB && db == xDB && dr == xDR && heads == xH)                             \
+    return Cfg<xNB, xDB, xDR, xH, xW, true, xBPW>::PAGE_REGS ? kPageLanes : kPageCache;
+  MLRA_MFMA_SHAPES(X)
+#undef X
+  return kPageCache;
+}
+
+int mfma_min_page_size(int nb, int db, int dr, int heads) {
+#define X(xNB, xDB, xDR, xH, xW, xBPW)                                                 \
+  if (nb == xNB && db == xDB && dr == xDR && heads == xH) {                           \
+    using CP = Cfg<xNB, xDB, xDR, xH, xW, true, xBPW>;                                \
+    return CP::PAGE_REGS ? CP::TPW : 1;                                               \
+  }
+  MLRA_MFMA_SHAPES(X)
+#undef X
+  return 1;
+}
 
 int mfma_stage_tokens(int nb, int db, int dr, int heads) {
 #define X(xNB, xDB, xDR, xH, xW, xBPW) \

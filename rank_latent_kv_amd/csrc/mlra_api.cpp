@@ -58,7 +58,6 @@ struct Topology {
 };
 constexpr Topology kLargestGfx950{};
 constexpr int kMaxSplits = 4096;
-constexpr int kPageCache = 256;
 
 struct Plan {
   int generic_reason = 0;   // MLRA_PLAN_* bits: why the generic kernel runs (0 on the MFMA path)
@@ -196,6 +195,10 @@ mlra_status make_plan(const mlra_decode_args* a, bool check_pointers, const Topo
       mfma = false;
       p.generic_reason |= MLRA_PLAN_GENERIC_ALIGNMENT;
     }
+    if (paged && a->page_size < mlra::mfma_min_page_size(a->num_branches, a->branch_dim, a->rope_dim, a->num_heads)) {
+      mfma = false;
+      p.generic_reason |= MLRA_PLAN_GENERIC_PAGE_SIZE;
+    }
   }
   if (!mfma && !mlra::generic_supported(a->num_branches, a->branch_dim, a->rope_dim))
     return fail(MLRA_ERR_UNSUPPORTED, "no kernel for num_branches=%d branch_dim=%d rope_dim=%d dtype=%d", a->num_branches,
@@ -236,8 +239,10 @@ mlra_status make_plan(const mlra_decode_args* a, bool check_pointers, const Topo
       split += p.stage;
   }
   if (paged && mfma) {
-    // the split's page ids must fit the kernel's LDS cache
-    const int64_t max_split = (int64_t)(kPageCache - 1) * a->page_size / p.stage * p.stage;
+    // the split's page ids must fit the kernel's page-id cache (one split starting mid-page
+    // spans one page more than its length needs)
+    const int cache = mlra::mfma_page_cache(a->num_branches, a->branch_dim, a->rope_dim, a->num_heads);
+    const int64_t max_split = (int64_t)(cache - 1) * a->page_size / p.stage * p.stage;
     if (max_split < p.stage) return fail(MLRA_ERR_UNSUPPORTED, "page_size %d too small for the MFMA path", a->page_size);
     // the kernel forms a page's byte offset as a 32 x 32 -> 64-bit product
     const int64_t page_bytes = (int64_t)a->page_size * a->row_stride * (a->dtype == MLRA_BF16 ? 2 : 4);

@@ -57,6 +57,10 @@ struct MfmaShape {
 };
 // Stage size in tokens of the MFMA kernel for this shape (0 if not built).
 int mfma_stage_tokens(int nb, int db, int dr, int heads);
+// Pages one split of the paged MFMA kernel of this shape may span.
+int mfma_page_cache(int nb, int db, int dr, int heads);
+// Smallest page size (tokens) the paged MFMA kernel of this shape takes.
+int mfma_min_page_size(int nb, int db, int dr, int heads);
 // Launch the MFMA attention kernel; returns hipSuccess or the launch error.
 hipError_t launch_attn_mfma(const AttnParams& p, bool paged, int grid_splits, hipStream_t stream);
 

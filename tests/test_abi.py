@@ -621,6 +621,27 @@ def test_plan_reports_the_generic_kernel_and_why():
     p = R.plan(a, cu_count=256)
     assert p["kernel"] == "generic" and p["generic_reasons"] == ["alignment"]
     assert p["work_groups"] == p["num_splits"] * 2 * 64   # one group per (split, sequence, head)
+    a = base_args()
+    a.page_table, a.max_pages, a.num_pages = FAKE * 64, 4096 // 8, 4096 // 8 * 2
+    a.page_size = 8               # MLRA-4's paged kernel moves 16-token blocks per wave from one page
+    p = R.plan(a, cu_count=256)
+    assert p["kernel"] == "generic" and p["generic_reasons"] == ["page_size"]
+    a.page_size, a.max_pages = 16, 4096 // 16
+    assert R.plan(a, cu_count=256)["kernel"] == "mfma"
+
+
+def test_paged_split_spans_at_most_the_page_id_cache():
+    """One long paged context on few CUs: the MLRA-4 split is capped so that it spans at most
+    the 64 page ids its kernel keeps in one register (a split may start mid-page)."""
+    lens = np.array([1 << 20], dtype=np.int32)
+    for ps in (16, 64, 1024):
+        a = base_args(B=1, L=1 << 20)
+        a.seq_lens_host = lens.ctypes.data
+        a.page_table, a.page_size = FAKE * 64, ps
+        a.max_pages = a.num_pages = (1 << 20) // ps
+        p = R.plan(a, cu_count=32)
+        assert p["kernel"] == "mfma"
+        assert -(-p["split_tokens"] // ps) + 1 <= 64
 
 
 def test_plan_rejects_bad_arguments():

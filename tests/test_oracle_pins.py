@@ -364,19 +364,32 @@ def _mutant(kind):
                 else:
                     e = np.exp(z - z.max(axis=1, keepdims=True))
                     pr = e / e.sum(axis=1, keepdims=True)
+                if kind == "shared_softmax":
+                    continue
                 u = pr @ cb
                 bw = (b + 1) % nb if kind == "wrong_wv_block" else b
                 Wb = w_v[:, :, bw * db:(bw + 1) * db]
+                if kind == "transposed_wv":          # W^V_{i,b} applied transposed (square blocks)
+                    Wb = Wb.transpose(0, 2, 1)
                 y[beta] += np.einsum("inj,ij->in", Wb, u)
+            if kind == "shared_softmax":            # one softmax over every branch's logits of a head
+                zs = np.concatenate([sm_scale * (q_lat[beta, :, b, :] @ C[:, b, :].T + rope) for b in range(nb)], 1)
+                e = np.exp(zs - zs.max(axis=1, keepdims=True))
+                pr = e / e.sum(axis=1, keepdims=True)
+                for b in range(nb):
+                    u = pr[:, b * L:(b + 1) * L] @ C[:, b, :]
+                    y[beta] += np.einsum("inj,ij->in", w_v[:, :, b * db:(b + 1) * db], u)
         a = 1.0 if kind == "no_alpha" else alpha
         return a * y
     return f
 
 
 @pytest.mark.parametrize("kind", ["drop_rope", "rope_sign", "strided_branch", "no_scale",
-                                  "softmax_over_heads", "wrong_wv_block", "no_alpha"])
+                                  "softmax_over_heads", "wrong_wv_block", "no_alpha", "shared_softmax",
+                                  "transposed_wv"])
 def test_planted_mistakes_are_caught(kind):
-    p = rand_problem(20, B=2, h=3, nb=4, db=3, dr=2, dh=4, lens=(6, 5))
+    # square W^V blocks (d_h = d_b) so that the transposed-W^V mutant is well formed
+    p = rand_problem(20, B=2, h=3, nb=4, db=4, dr=2, dh=4, lens=(6, 5))
     mutant = _mutant(kind)
     y = mutant(p["q_lat"], p["q_rope"], p["kv_lat"], p["kv_rope"], p["seq_lens"], p["w_v"], p["sm_scale"],
                p["alpha"])
@@ -386,6 +399,26 @@ def test_planted_mistakes_are_caught(kind):
     assert rel(y, ref_sdpa) > 1e-3 or rel(y, ref_bf) > 1e-3
     # and the oracle itself passes both
     assert rel(absorbed(p), ref_sdpa) < 1e-12 and rel(absorbed(p), ref_bf) < 1e-12
+
+
+def test_block_identity():
+    """Branch slicing ([MLRA] §二, reading A5): with branch b owning latent columns
+    [b*d_b, (b+1)*d_b), the branch dot products q~_b . c_b sum to the full-width q~ . c; the
+    oracle run with the whole latent as one branch is MLA decode (which never slices), and
+    with four branches (independent softmaxes) it is not."""
+    p = rand_problem(23, B=2, h=3, nb=4, db=5, dr=3, dh=7, lens=(9, 6))
+    B, h, nb, db = p["q_lat"].shape
+    dc = nb * db
+    z_blocks = np.einsum("bhnd,bsnd->bhs", p["q_lat"], p["kv_lat"].reshape(B, -1, nb, db))
+    z_full = np.einsum("bhc,bsc->bhs", p["q_lat"].reshape(B, h, dc), p["kv_lat"])
+    assert np.max(np.abs(z_blocks - z_full)) < 1e-12
+    y_mla = O.mla_decode(p["q_lat"].reshape(B, h, 1, dc), p["q_rope"], p["kv_lat"], p["kv_rope"], p["seq_lens"],
+                         p["w_v"], p["sm_scale"], p["alpha"])
+    # MLA over the full latent == per-branch attention only when there is one branch
+    one = O.mlra_decode_absorbed(p["q_lat"].reshape(B, h, 1, dc), p["q_rope"], p["kv_lat"], p["kv_rope"],
+                                 p["seq_lens"], p["w_v"], p["sm_scale"], p["alpha"])
+    assert rel(one, y_mla) < 1e-12
+    assert rel(absorbed(p), y_mla) > 1e-3
 
 
 def test_bruteforce_on_tiny_f32_workload():
