@@ -200,6 +200,23 @@ mlra_status mlra_decode_plan(const mlra_decode_args* args, int32_t cu_count, mlr
 mlra_status mlra_decode(const mlra_decode_args* args, void* stream);
 
 /*
+ * For callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): mlra_decode with the
+ * split-partials workspace taken from a device array inside the library instead of
+ * args->workspace (which is ignored). The array is MLRA_NOALLOC_SCRATCH_BYTES
+ * (16 MiB) per GPU, allocated when the library's code is loaded on that GPU and
+ * held until the process ends; the call itself allocates nothing. Its device
+ * address is looked up once per device on the first call there. Every call on one
+ * GPU uses the same array: calls that overlap on one GPU (other streams, other
+ * threads) race, so the caller serialises them. Nothing in it needs clearing
+ * between calls (each call writes every record it reads). Errors: as mlra_decode,
+ * plus MLRA_ERR_WORKSPACE (nothing enqueued) when the call's split state exceeds the
+ * array.
+ */
+#define MLRA_NOALLOC_SCRATCH_BYTES (16u << 20)
+mlra_status mlra_decode_noalloc(const mlra_decode_args* args, void* stream);
+
+/*
  * MLA decode ([MLRA] §1.3): the single-latent comparison path. Same arguments;
  * requires num_branches == 1 (branch_dim is then the latent width d_c).
  */

@@ -33,6 +33,7 @@ EXPORTED_SYMBOLS = (
     "mla_decode", "mlra_paged_append", "mlra_paged_gather", "mlra_page_table_check", "mlra_page_pool_create",
     "mlra_page_pool_alloc", "mlra_page_pool_free", "mlra_page_pool_num_free", "mlra_page_pool_destroy",
     "mlra_decode_prepare", "mlra_read_probe_words", "mlra_read_probe", "mlra_decode_plan",
+    "mlra_decode_noalloc",
 )
 MLRA_KERNEL_MFMA = 0
 MLRA_KERNEL_GENERIC = 1
@@ -112,6 +113,7 @@ def lib() -> ctypes.CDLL:
         L.mlra_decode_validate.argtypes = [P(DecodeArgs)]
         L.mlra_decode.argtypes = [P(DecodeArgs), vp]
         L.mla_decode.argtypes = [P(DecodeArgs), vp]
+        L.mlra_decode_noalloc.argtypes = [P(DecodeArgs), vp]
         L.mlra_decode_prepare.argtypes = [P(PrepareArgs), vp]
         L.mlra_paged_append.argtypes = [vp, i64, i32, i32, i32, vp, i32, vp, vp, i32, i32, vp, vp]
         L.mlra_paged_gather.argtypes = [vp, i64, i32, i32, i32, vp, i32, vp, i32, i32, i32, vp, vp, vp]
@@ -127,7 +129,7 @@ def lib() -> ctypes.CDLL:
         L.mlra_read_probe_words.restype = i32
         L.mlra_read_probe.argtypes = [vp, ctypes.c_size_t, vp, i32, vp]
         L.mlra_decode_plan.argtypes = [P(DecodeArgs), i32, P(PlanInfo)]
-        for name in ("mlra_decode_validate", "mlra_decode", "mla_decode", "mlra_decode_prepare", "mlra_paged_append",
+        for name in ("mlra_decode_validate", "mlra_decode", "mla_decode", "mlra_decode_noalloc", "mlra_decode_prepare", "mlra_paged_append",
                      "mlra_paged_gather", "mlra_page_table_check", "mlra_page_pool_create",
                      "mlra_page_pool_alloc", "mlra_page_pool_free", "mlra_read_probe", "mlra_decode_plan"):
             getattr(L, name).restype = i32
@@ -320,6 +322,17 @@ def _run(fn_name: str, q_lat, q_rope, kv_lat, kv_rope, seq_lens, w_v, *, sm_scal
 def decode(q_lat, q_rope, kv_lat, kv_rope, seq_lens, w_v, *, sm_scale: float, alpha: float, **kw) -> torch.Tensor:
     """MLRA decode (any number of branches). Returns y [B, h, d_h]."""
     return _run("mlra_decode", q_lat, q_rope, kv_lat, kv_rope, seq_lens, w_v, sm_scale=sm_scale, alpha=alpha, **kw)
+
+
+def decode_noalloc(q_lat, q_rope, kv_lat, kv_rope, seq_lens, w_v, *, sm_scale: float, alpha: float, out: torch.Tensor,
+                   stream=None, **kw) -> torch.Tensor:
+    """``mlra_decode_noalloc``: the decode with the library's own device scratch (no workspace,
+    no device allocation in the call; ``out`` must be given). Calls that overlap on one GPU race."""
+    if not q_lat.is_cuda:
+        raise ValueError("the decode runs on the GPU: pass device tensors (q_lat is on the CPU)")
+    args = make_args(q_lat, q_rope, kv_lat, kv_rope, seq_lens, w_v, sm_scale=sm_scale, alpha=alpha, out=out, **kw)
+    _check(lib().mlra_decode_noalloc(ctypes.byref(args), _stream_handle(stream)))
+    return out
 
 
 def mla_decode(q_lat, q_rope, kv_lat, kv_rope, seq_lens, w_v, *, sm_scale: float, alpha: float = 1.0,

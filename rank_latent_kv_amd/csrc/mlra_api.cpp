@@ -7,10 +7,11 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
-#include <hip/hip_runtime_api.h>
+#include <hip/hip_runtime.h>
 
 #include "mlra.h"
 #include "mlra_internal.h"
@@ -307,6 +308,36 @@ Topology current_topology() {
   return t;
 }
 
+// Scratch of the allocation-free decode entry point: the split-partials workspace in a
+// file-scope device array, one per GPU, held until the process ends. In host code `scratch`
+// names a host-side stand-in, not a device address: its address on a device comes from
+// hipGetSymbolAddress, taken once per device with that device current, and only that
+// pointer is ever passed to kernels.
+constexpr size_t kScratchBytes = MLRA_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) char scratch[kScratchBytes];
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+mlra_status scratch_of_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(MLRA_ERR_UNSUPPORTED, "device %d is beyond the library's %d devices", dev, kMaxDevices);
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (!p) {
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+      if (!p) return fail(MLRA_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+      g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return MLRA_OK;
+}
+
 mlra_status run_decode(const mlra_decode_args* a, void* stream_v) {
   Plan plan;
   mlra_status st = make_plan(a, true, current_topology(), &plan);
@@ -435,6 +466,25 @@ mlra_status mlra_decode_validate(const mlra_decode_args* args) {
 }
 
 mlra_status mlra_decode(const mlra_decode_args* args, void* stream) { return run_decode(args, stream); }
+
+mlra_status mlra_decode_noalloc(const mlra_decode_args* args, void* stream) {
+  if (!args) return fail(MLRA_ERR_INVALID_ARG, "args is NULL");
+  Plan plan;
+  mlra_status st = make_plan(args, true, current_topology(), &plan);
+  if (st != MLRA_OK) return st;
+  if (plan.ws_bytes > kScratchBytes)
+    return fail(MLRA_ERR_WORKSPACE,
+                "this call needs %zu bytes of split state, beyond the %zu-byte device array of the allocation-free "
+                "entry point (use mlra_decode with a workspace)",
+                plan.ws_bytes, kScratchBytes);
+  void* p = nullptr;
+  st = scratch_of_current_device(&p);
+  if (st != MLRA_OK) return st;
+  mlra_decode_args a = *args;
+  a.workspace = p;
+  a.workspace_bytes = kScratchBytes;
+  return run_decode(&a, stream);
+}
 
 mlra_status mla_decode(const mlra_decode_args* args, void* stream) {
   if (!args) return fail(MLRA_ERR_INVALID_ARG, "args is NULL");
