@@ -47,11 +47,38 @@ PMC_SUMMARY = os.path.join(ROOT, "profiles", "pmc_traffic.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "rank_latent_kv_amd", "csrc", f) for f in ("attn_mfma.hip", "mlra_api.cpp")]
 
 
+def code_tokens(text: str) -> str:
+    """C++ source without its comments and with whitespace collapsed: what the compiler sees,
+    so that a comment edit does not void the stored counter figures. String literals are kept
+    whole (a "//" inside one is not a comment)."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if c == '"' or c == "'":
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def kernel_source_hash() -> str:
+    """Hash of the attention kernel's and the planner's code (comments and whitespace ignored)."""
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
-        with open(f, "rb") as fh:
-            h.update(fh.read())
+        with open(f, encoding="utf-8") as fh:
+            h.update(code_tokens(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -23,8 +23,9 @@
 //   softmax lazy running max: the reference m is the exact max of the split's first
 //           sub-tile and only moves (with a rescale of O and l) when a sub-tile's
 //           weights sum past 2^16; p = 2^(x-m) is packed to bf16 and l accumulates the
-//           packed values with a bf16 dot2, so the normaliser sums exactly the weights
-//           the P.C product uses;
+//           packed values (4x4x4 bf16 MFMAs with an all-ones operand add four of a lane's
+//           weights at a time), so the normaliser sums exactly the weights the P.C
+//           product uses;
 //   values  O^T[feat x head] += C_b^T[feat x tok] . P^T[tok x head], MFMA, with the
 //           transposed latent read by ds_read_b64_tr_b16.
 // The loop is software-pipelined: the score MFMAs of the next sub-tile go out before the

@@ -72,3 +72,14 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=300, cwd=ROOT)
     assert r.returncode != 0
     assert "one GPU" in (r.stdout + r.stderr)
+
+
+def test_kernel_hash_ignores_comments_and_whitespace():
+    """The stored counter figures stay valid across comment edits, not across code edits."""
+    code = 'int f(int x) {  // doubles\n  /* note */ return 2 * x; }\nconst char* s = "a // b";\n'
+    same = 'int f(int x) {\n  return 2 * x;   // twice\n}\nconst char* s = "a // b";\n'
+    other = 'int f(int x) { return 3 * x; }\nconst char* s = "a // b";\n'
+    assert bench.code_tokens(code) == bench.code_tokens(same)
+    assert bench.code_tokens(code) != bench.code_tokens(other)
+    assert '"a // b"' in bench.code_tokens(code)
+

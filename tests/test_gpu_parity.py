@@ -214,6 +214,23 @@ def test_error_flag_for_long_seq_len():
     assert row_rel_err(f64(y), ref) <= TOL_BF16
 
 
+@pytest.mark.parametrize("preset,mla", [("mlra4_b16_l32k", False), ("mla_b16_l32k", True),
+                                        ("mlra4_tp_shard_b64_l64k", False)])
+def test_device_lengths_below_the_host_copy(preset, mla):
+    """The host copy says every sequence holds 3000 rows (and they exist), so each split's first
+    stage below row 3000 is read before the device length arrives. The device lengths are
+    shorter: 100 rows (a ragged first stage, read again over the same slots, and empty splits
+    that leave early), 2500 (a ragged last split) and 129 (a one-row split). The output must
+    follow the device lengths."""
+    w = PRESETS[preset].replace(batch=3)
+    inp = make_inputs(w, seq_lens=[3000, 3000, 3000])
+    dev_lens = [100, 2500, 129]
+    say(f"{preset}: device lengths {dev_lens} below the host copy 3000")
+    y = gpu_decode(w, inp, mla=mla, seq_lens_dev=torch.tensor(dev_lens, dtype=torch.int32, device=DEV))
+    ref = oracle_decode(w, dict(inp, seq_lens=torch.tensor(dev_lens, dtype=torch.int32)))
+    assert row_rel_err(f64(y), ref) <= TOL_BF16
+
+
 def test_caller_workspace_reuse():
     w = PRESETS["mlra4_b16_l32k"].replace(batch=2)
     inp = make_inputs(w, seq_lens=[3000, 3000])
