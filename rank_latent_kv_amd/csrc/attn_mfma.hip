@@ -61,6 +61,7 @@ constexpr int kSubPerStage = 4;            // 32-token sub-tiles per stage (more
 constexpr int kLdsBytes = 160 * 1024;
 constexpr int kPageCache = 256;            // page ids of one split kept in LDS (paged mode)
 constexpr int kPageLanes = 64;             // or in one register, one page id per lane
+constexpr int kRotateStages = 64;          // splits of at least this many full stages rotate their start
 constexpr float kRescaleThreshold = 8.0f;  // log2 units: p = 2^x stays <= 256
 constexpr float kStageSumMax = 65536.0f;   // a lane's sub-tile weights summing past this trigger the exact max
 
@@ -331,8 +332,12 @@ __global__ __launch_bounds__(W * 64, 1) void attn_mfma_kernel(AttnParams p) {
   const uint32_t page_bytes32 = (uint32_t)page_bytes;
   const int64_t stage_bytes_g = (int64_t)C::ST * p.row_stride_b;
 
+  // Full stage s of the split holds cache stage (s + rot) mod nrot (set below for long splits;
+  // the identity otherwise); a ragged last stage stays last.
+  int rot = 0, nrot = 1;
   auto issue_stage = [&](int s) __attribute__((always_inline)) {
-    const int tok0 = t0 + s * C::ST;
+    const int ps = s < nrot ? (s + rot) % nrot : s;
+    const int tok0 = t0 + ps * C::ST;
     const uint32_t ring = smem_lds + (uint32_t)((s % C::NS) * C::STAGE_BYTES);
     if (tok0 + C::ST <= t1) {
       // full stage: one pointer add (and for small pages one LDS page-id read) per DMA
@@ -373,7 +378,7 @@ __global__ __launch_bounds__(W * 64, 1) void attn_mfma_kernel(AttnParams p) {
 #pragma unroll
         for (int i = 0; i < C::DMA_HI; ++i) {
           if (i >= ndma) break;
-          dma16(dptr[i] + (int64_t)s * stage_bytes_g, __builtin_amdgcn_readfirstlane(slot0 + (uint32_t)(C::DW * i * 1024)));
+          dma16(dptr[i] + (int64_t)ps * stage_bytes_g, __builtin_amdgcn_readfirstlane(slot0 + (uint32_t)(C::DW * i * 1024)));
         }
       }
     } else {
@@ -654,6 +659,15 @@ __global__ __launch_bounds__(W * 64, 1) void attn_mfma_kernel(AttnParams p) {
 
   // ---- main loop: full stages (the first seeds the running max), ragged last stage ----------
   const int nfull = (t1 - t0) / C::ST;       // stages with ST valid tokens
+  // Long splits stream their full stages from a per-sequence starting stage (37 beta mod n).
+  // Sequences whose caches lie a large power-of-two multiple apart otherwise read in lockstep
+  // and collide in the same HBM channels: the 16-head MLA shard (64 sequences of 20 MiB, four
+  // 5 MiB splits each) ran 229 -> 197 us. On 16-stage splits the rotation cost 2-3%, so only
+  // long splits rotate. The sum over a split's tokens is order-dependent only in rounding.
+  if (nfull >= kRotateStages) {
+    nrot = nfull;
+    rot = (int)(((unsigned)beta * 37u) % (unsigned)nfull);
+  }
   // With one branch per wave the loop is software-pipelined over this wave's sub-tiles
   // k = 0, 1, ... of the full stages: the score MFMAs of sub-tile k + 1 are issued before
   // the softmax of sub-tile k, so the matrix cores work while the vector ALUs

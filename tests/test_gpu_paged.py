@@ -123,6 +123,27 @@ def test_paged_equals_contiguous_bitwise_mla():
         assert torch.equal(a, b), ns
 
 
+def test_long_splits_rotate_their_stage_order():
+    """Splits of 64 or more full stages start at a per-sequence stage and wrap around. One
+    split per sequence of 8,229-12,000 tokens (64-93 full stages and a ragged tail): the
+    output follows the oracle, and the paged and contiguous instances, which rotate alike,
+    still agree bit for bit (MLA: its page ids of up to 255 pages per split sit in LDS)."""
+    w = PRESETS["mla_b16_l32k"].replace(batch=3, paged=True, page_size=64, name="mla_paged_long")
+    lens = [8229, 12000, 8192]
+    inp = make_inputs(w, seq_lens=lens)
+    wc = w.replace(paged=False)
+    say(f"rotated long splits, MLA lens {lens}")
+    a = gpu_decode(w, inp, num_splits=1, mla=True)
+    b = gpu_decode(wc, gather_contiguous(w, inp), num_splits=1, mla=True)
+    assert torch.equal(a, b)
+    assert row_rel_err(f64(a), oracle_decode(w, inp)) <= 1e-2
+    w4 = PRESETS["mlra4_b16_l32k"].replace(batch=3)
+    inp4 = make_inputs(w4, seq_lens=lens)
+    say(f"rotated long splits, MLRA-4 lens {lens}")
+    y = gpu_decode(w4, inp4, num_splits=1)
+    assert row_rel_err(f64(y), oracle_decode(w4, inp4)) <= 1e-2
+
+
 def test_append_and_gather_bitexact():
     rng = np.random.default_rng(3)
     ps, P, Rw = 64, 37, 160
