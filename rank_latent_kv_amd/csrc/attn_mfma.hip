@@ -795,6 +795,16 @@ __global__ __launch_bounds__(W * 64, 1) void attn_mfma_kernel(AttnParams p) {
                        f32x16 (&nxt)[C::HPW][BPW], bf16x2 (&pkc)[C::HPW][BPW][8],
                        bf16x2 (&pkp)[C::HPW][BPW][8]) __attribute__((always_inline)) {
         constexpr bool NXT = decltype(nxt_c)::value, PREV = decltype(prev_c)::value;
+        // The two waves of a SIMD (branch groups 0 and 1) meet at every stage barrier. The
+        // sequencer issues the older wave first, so the younger one used to finish its stage
+        // alone; raising its priority for the stage's first step and levelling it for the
+        // second lets both end together (1.6% per headline call, 0.7% paged).
+        if constexpr (decltype(boundary_c)::value) {
+          if (bg == 1) __builtin_amdgcn_s_setprio(1);
+          else __builtin_amdgcn_s_setprio(0);
+        } else {
+          __builtin_amdgcn_s_setprio(0);
+        }
         if constexpr (NXT && decltype(boundary_c)::value) begin_piped((k + 1) / C::NSW);
         if constexpr (NXT) scores(sub_of(k + 1), nxt);
         if constexpr (PREV) pv_all(k - 1, pkp);
