@@ -108,6 +108,12 @@ PRESETS: Dict[str, Workload] = {
                                       branch_dim=128, rope_dim=32, head_dim=128, seq_len=65536,
                                       sm_scale=1.0 / math.sqrt(160.0), alpha=1.0,
                                       value_std=1.0 / 8.0, seed_offset=5),
+    # the rank of the branch-sharded design: all 64 heads over the one 32-wide latent block it
+    # holds, plus the replicated RoPE key (the rank runs the kernel with one branch and applies
+    # alpha * W^V of its branch; the ranks' outputs are then summed)
+    "mlra4_branch_shard_b64_l64k": Workload("mlra4_branch_shard_b64_l64k", batch=64, heads=64, branches=1,
+                                            branch_dim=32, rope_dim=32, head_dim=128, seq_len=65536,
+                                            sm_scale=1.0 / 8.0, alpha=0.5, seed_offset=7),
 }
 
 

@@ -39,6 +39,7 @@ def check_sampled(w, inp, seqs, **kw):
     ("mlra4_paged_b4_l64k_128k", False, None),
     ("mlra4_tp_shard_b64_l64k", False, list(range(0, 64, 4)) + [63]),
     ("mla_tp_shard_b64_l64k", True, list(range(0, 64, 8)) + [63]),
+    ("mlra4_branch_shard_b64_l64k", False, list(range(0, 64, 8)) + [63]),
 ])
 def test_benchmark_workload_full_size(preset, mla, seqs):
     w = PRESETS[preset]
