@@ -41,6 +41,7 @@ PLAN_GENERIC_DTYPE = 1
 PLAN_GENERIC_SHAPE = 2
 PLAN_GENERIC_ALIGNMENT = 4
 PLAN_GENERIC_PAGE_SIZE = 8
+NOALLOC_SCRATCH_BYTES = 16 << 20   # MLRA_NOALLOC_SCRATCH_BYTES: the allocation-free entry point's device array
 
 
 class MlraError(RuntimeError):

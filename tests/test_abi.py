@@ -161,6 +161,28 @@ def test_workspace_errors():
     assert R.validate(a) == R.MLRA_ERR_INVALID_ARG
 
 
+def test_noalloc_refuses_on_the_host_first():
+    """mlra_decode_noalloc checks its arguments and the size of the split state on the host
+    before any device call: a NULL struct and invalid fields are refused, and so is a plan whose
+    split state exceeds the library's device array (here without a GPU in the process)."""
+    L = R.lib()
+    assert L.mlra_decode_noalloc(None, None) == R.MLRA_ERR_INVALID_ARG
+    a = base_args()
+    a.num_heads = 0
+    assert L.mlra_decode_noalloc(ctypes.byref(a), None) == R.MLRA_ERR_INVALID_ARG
+    big = base_args(B=256, L=8192)
+    big.num_splits = 64
+    assert R.workspace_size(big) > R.NOALLOC_SCRATCH_BYTES
+    assert L.mlra_decode_noalloc(ctypes.byref(big), None) == R.MLRA_ERR_WORKSPACE
+    assert "device array" in R.last_error()
+
+
+def test_noalloc_array_size_matches_the_header():
+    text = open(os.path.join(ROOT, "include", "mlra.h")).read()
+    m = re.search(r"#define MLRA_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == R.NOALLOC_SCRATCH_BYTES
+
+
 def test_overlapping_rope_rejected():
     a = with_workspace(base_args())
     a.kv_rope = a.kv_lat + 2 * 64
