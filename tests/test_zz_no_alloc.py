@@ -70,3 +70,45 @@ def test_noalloc_refuses_split_state_beyond_its_array():
     assert e.value.status == R.MLRA_ERR_WORKSPACE and "device array" in str(e.value)
     torch.cuda.synchronize()
     assert bool(torch.all(out == 7.0))
+
+
+def test_noalloc_under_graph_capture():
+    """The caller the entry point exists for: a decode captured into a HIP graph (no device
+    allocation is allowed while capturing). The graph is replayed several times, with the
+    program's own eager work and a synchronisation between replays, and every replay must
+    equal the eager call bit for bit."""
+    w = PRESETS["mlra4_b16_l32k"].replace(batch=3)
+    lens = [5000, 1200, 3333]
+    inp = make_inputs(w, seq_lens=lens)
+    d = {k: v.to(DEV) for k, v in inp.items()}
+    dc = w.latent_dim
+    kv = d["kv"]
+    lens_host = inp["seq_lens"].to(torch.int32).contiguous()
+    out = torch.empty((w.batch, w.heads, w.head_dim), dtype=torch.bfloat16, device=DEV)
+
+    def call():
+        R.decode_noalloc(d["q_lat"], d["q_rope"], kv[..., :dc], kv[..., dc:], d["seq_lens"], d["w_v"],
+                         sm_scale=w.sm_scale, alpha=w.alpha, out=out, seq_lens_host=lens_host)
+
+    say("noalloc: eager reference, then capture")
+    call()
+    torch.cuda.synchronize()
+    ref = out.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            call()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for r in range(4):
+        out.fill_(float("nan"))
+        junk = torch.randn(1 << 20, device=DEV).sum()     # eager work between the replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        say(f"noalloc graph replay {r}")
+        assert torch.equal(out, ref), r
+        assert bool(torch.isfinite(junk))
+    assert row_rel_err(f64(out), oracle_decode(w, inp)) <= TOL_BF16
