@@ -25,7 +25,8 @@
  * Conventions for every entry point:
  *   - Device pointers are HIP device memory on the current device; "host" marks
  *     host memory. The caller owns every buffer; the library keeps no pointer
- *     past the call and allocates no device memory.
+ *     past the call and allocates no device memory. Its one device buffer is the
+ *     array of mlra_decode_noalloc, which comes with the library's code.
  *   - Work is enqueued on the given stream (NULL = the default stream) and the
  *     call returns without waiting. Calls that overlap on one workspace race.
  *   - Nothing throws across the ABI. Every failure returns a status and sets a
