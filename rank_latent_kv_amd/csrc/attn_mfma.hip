@@ -77,14 +77,13 @@ struct Cfg {
   static constexpr int P = WPB / HGSPLIT;                // token phases
   static constexpr int SUB = P > kSubPerStage ? P : kSubPerStage;     // 32-token sub-tiles per stage
   static constexpr int NSW = SUB / P;                    // sub-tiles of one wave per stage
-  // one branch per wave: the next sub-tile's scores are issued before the current softmax;
-  // with several branches per wave their score tiles leave no registers for that
+  // one branch per wave: the next sub-tile's scores are issued before the current softmax
   static constexpr bool PIPE = BPW == 1;
-  // several branches per wave with two waves per SIMD: the registers hold two sub-tiles'
-  // scores, so the scores of sub-tile k + 1 and the P.C of sub-tile k - 1 are issued in
-  // the same block as the softmax of sub-tile k. The delayed P.C keeps a stage's ring slot
-  // in use until two barriers later, which needs a ring of four stages (the paged instance,
-  // whose page ids leave room for three, runs the same work split unpipelined).
+  // several branches per wave with two waves per SIMD (PIPE2, below): the registers hold two
+  // sub-tiles' scores, so the scores of sub-tile k + 1 and the P.C of sub-tile k - 1 are
+  // issued in the same block as the softmax of sub-tile k. The delayed P.C keeps a stage's
+  // ring slot in use until two barriers later, which needs a ring of four stages; with more
+  // waves (fewer registers each) or a shallower ring the same work split runs unpipelined.
   static constexpr int ST = 32 * SUB;                    // tokens per stage
   static constexpr int NCL = NB * DB / 8;                // latent 16-byte chunks per row
   static constexpr int NCR = DR / 8;                     // RoPE 16-byte chunks per row
@@ -676,7 +675,7 @@ __global__ __launch_bounds__(W * 64, 1) void attn_mfma_kernel(AttnParams p) {
   // s - 2: LOOK = NS - 2 stages ahead. Without the pipelining every wave is done with stage
   // s - 1 when it passes stage s's barrier, so any slot but stage s's may be refilled; two
   // stages ahead measured best there (three ahead was slower on a 4-stage ring, one ahead
-  // much slower on the 3-stage ring of the paged instance).
+  // much slower on a 3-stage ring).
   constexpr int LOOK = (C::PIPE || C::PIPE2) ? C::NS - 2 : 2;
   // stage 0 first, then the queries (into the last ring slot, which the prologue's stages do
   // not use: LOOK <= NS - 1), then the rest of the prologue's stages
