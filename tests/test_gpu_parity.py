@@ -231,6 +231,23 @@ def test_device_lengths_below_the_host_copy(preset, mla):
     assert row_rel_err(f64(y), ref) <= TOL_BF16
 
 
+@pytest.mark.parametrize("preset,out_dtype", [("mlra4_b16_l32k", torch.bfloat16), ("tiny_f32", torch.float32)])
+def test_empty_device_lengths_give_zero_rows(preset, out_dtype):
+    """Device lengths of 0 and below are clamped to an empty context and flagged: those
+    sequences' outputs are exact zeros (no token contributes, nothing is NaN), and the other
+    sequences are unaffected (matrix-core path and generic fp32 path)."""
+    w = PRESETS[preset].replace(batch=3)
+    inp = make_inputs(w, seq_lens=[200, 200, 200])
+    flags = torch.zeros(1, dtype=torch.int32, device=DEV)
+    bad = torch.tensor([0, -5, 200], dtype=torch.int32, device=DEV)
+    say(f"{preset}: device lengths 0 and -5")
+    y = gpu_decode(w, inp, host_lens=False, seq_lens_dev=bad, error_flags=flags, out_dtype=out_dtype)
+    assert int(flags.item()) & R.FLAG_SEQ_LEN_CLAMPED
+    assert bool(torch.all(y[:2] == 0))
+    tol = TOL_F32 if out_dtype == torch.float32 else TOL_BF16
+    assert row_rel_err(f64(y[2:]), oracle_decode(w, inp, seqs=[2])) <= tol
+
+
 def test_caller_workspace_reuse():
     w = PRESETS["mlra4_b16_l32k"].replace(batch=2)
     inp = make_inputs(w, seq_lens=[3000, 3000])
