@@ -921,15 +921,20 @@ __global__ __launch_bounds__(W * 64, 1) void attn_mfma_kernel(AttnParams p) {
 
   // Rows [r0, r0 + nr) of every output tile of this wave, and (with ml) its (m, l), into the
   // split's record. A lane's rows 4j..4j+3 are 4 consecutive features. With `through`, the values
-  // were written by VALU instructions and go out through the write-through asm stores.
+  // were written by VALU instructions and may go out through the write-through asm stores. Only
+  // stores that fill whole 32-byte pieces do: a lane pair's 4-row stores, and the (m, l) pairs
+  // when there is one branch (then 32 heads' pairs are contiguous). Narrower pieces (2-row
+  // stores, (m, l) pairs interleaved by branch) stay in L2, which merges them into lines:
+  // written through, each became a partial write of its own (1.5 MB more at the MLRA-4
+  // headline; the 16-head MLRA-4 shard +0.4% per call, MLA +1.0% with its pairs held back).
   auto store_rows = [&](int r0, int nr, bool ml, auto through_c) __attribute__((always_inline)) {
     constexpr bool through = decltype(through_c)::value;
     auto put4 = [&](float* dst, float a, float b, float c, float d) __attribute__((always_inline)) {
       if constexpr (through) store_through4(dst, a, b, c, d);
       else *reinterpret_cast<float4*>(dst) = make_float4(a, b, c, d);
     };
-    auto put2 = [&](float* dst, float a, float b) __attribute__((always_inline)) {
-      if constexpr (through) store_through2(dst, a, b);
+    auto put_ml = [&](float* dst, float a, float b) __attribute__((always_inline)) {
+      if constexpr (through && NB == 1) store_through2(dst, a, b);
       else *reinterpret_cast<float2*>(dst) = make_float2(a, b);
     };
 #pragma unroll
@@ -953,11 +958,12 @@ __global__ __launch_bounds__(W * 64, 1) void attn_mfma_kernel(AttnParams p) {
 #pragma unroll
             for (int r = 0; r < 16; r += 2) {
               if (r != r0) continue;
-              put2(o + 32 * mt + 8 * (r / 4) + 4 * g + (r % 4), acc[h][bb][mt][r], acc[h][bb][mt][r + 1]);
+              *reinterpret_cast<float2*>(o + 32 * mt + 8 * (r / 4) + 4 * g + (r % 4)) =
+                  make_float2(acc[h][bb][mt][r], acc[h][bb][mt][r + 1]);
             }
           }
         }
-        if (ml && g == 0) put2(p.ws_ml + rec * 2, mref[h][bb], lsum[h][bb]);
+        if (ml && g == 0) put_ml(p.ws_ml + rec * 2, mref[h][bb], lsum[h][bb]);
       }
     }
   };
