@@ -40,6 +40,17 @@ def test_event_pass_brackets_every_sample_once_after_its_warmup(samples):
     assert all(a is b for a, b in zip(tail[0::2], ev)) and all(any(c is p for p in plain) for c in tail[1::2])
 
 
+def test_timing_events_drop_the_system_fence():
+    """The roofline events are created with hipEventDisableSystemFence: the flag value bench.py
+    passes is the one the installed HIP header defines."""
+    import re
+    hdr = "/opt/rocm/include/hip/hip_runtime_api.h"
+    if not os.path.exists(hdr):
+        pytest.skip("no HIP headers on this host")
+    m = re.search(r"#define\s+hipEventDisableSystemFence\s+(0x[0-9a-fA-F]+)", open(hdr).read())
+    assert m and int(m.group(1), 16) == bench.HIP_EVENT_DISABLE_SYSTEM_FENCE
+
+
 def test_driver_style_run_gets_twenty_event_samples():
     src = open(os.path.join(ROOT, "bench.py")).read()
     assert "n_ev = max(20, args.event_samples)" in src
