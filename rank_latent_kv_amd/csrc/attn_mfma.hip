@@ -31,8 +31,9 @@
 // The loop is software-pipelined: the score MFMAs of the next sub-tile go out before the
 // softmax of the current one (with several branches per wave, together with the P.C MFMAs of
 // the previous sub-tile, interleaved with the softmax's vector instructions).
-// Each split writes its unnormalised (o, m, l); the merge kernel combines the splits
-// (log-sum-exp) and applies W^V per branch.
+// Each split writes its unnormalised (o, m, l), through L2 to memory where a store fills whole
+// 32-byte pieces; the merge kernel combines the splits (log-sum-exp) and applies W^V per
+// branch.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
