@@ -154,7 +154,7 @@ __global__ __launch_bounds__(kThreads) void attn_generic_kernel(AttnParams p) {
   for (int k = 0; k < kMaxE; ++k) {
     const int e = tid + k * kThreads;
     if (e >= DC) break;
-    p.ws_o[rec0 * DB + e] = o[k];
+    static_cast<float*>(p.ws_o)[rec0 * DB + e] = o[k];
   }
   if (tid < NB) {
     p.ws_ml[(rec0 + tid) * 2] = mst[tid];

@@ -99,7 +99,8 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeParams p) {
       const float* w = wts + (bl * p.NB + b) * S;
       for (int s = 0; s < nsplit[bl]; ++s) {
         const int64_t rec = (((int64_t)beta * S + s) * p.H + head) * p.NB + b;
-        acc += w[s] * p.ws_o[rec * p.DB + f];
+        acc += w[s] * (p.ws_o_f16 ? (float)static_cast<const _Float16*>(p.ws_o)[rec * p.DB + f]
+                                  : static_cast<const float*>(p.ws_o)[rec * p.DB + f]);
       }
     }
     u[idx] = acc;
@@ -137,7 +138,9 @@ typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 
 constexpr int kChunk = 8;   // splits whose loads are issued together per thread
 
-template <int DC, int DH, int SEQB>
+// F16: the output records are scaled fp16 (the scale is already in m and l). A compile-time
+// choice, so that every split's loads still go out together before the first is used.
+template <int DC, int DH, int SEQB, bool F16>
 __global__ __launch_bounds__(kMergeThreads) void merge_mfma_kernel(MergeParams p) {
   constexpr int KC = DC / 32;                      // K-chunks of the epilogue
   constexpr int NT = DH / 16;                      // 16-wide output tiles
@@ -178,7 +181,16 @@ __global__ __launch_bounds__(kMergeThreads) void merge_mfma_kernel(MergeParams p
       const float2 ml = *reinterpret_cast<const float2*>(p.ws_ml + rec * 2);
       mv[j] = ml.x;
       lv[j] = ml.y;
-      ov[j] = *reinterpret_cast<const float4*>(p.ws_o + rec * DB + (k - b * DB));
+      const int64_t oi = rec * DB + (k - b * DB);
+      if constexpr (F16) {
+        const uint2 w = *reinterpret_cast<const uint2*>(static_cast<const _Float16*>(p.ws_o) + oi);
+        ov[j] = make_float4((float)__builtin_bit_cast(_Float16, (unsigned short)(w.x & 0xffffu)),
+                            (float)__builtin_bit_cast(_Float16, (unsigned short)(w.x >> 16)),
+                            (float)__builtin_bit_cast(_Float16, (unsigned short)(w.y & 0xffffu)),
+                            (float)__builtin_bit_cast(_Float16, (unsigned short)(w.y >> 16)));
+      } else {
+        ov[j] = *reinterpret_cast<const float4*>(static_cast<const float*>(p.ws_o) + oi);
+      }
     }
   };
   // Order of the requests: the sequence length and the first round of partials, then the
@@ -334,9 +346,15 @@ hipError_t launch_merge(const MergeParams& p, hipStream_t stream) {
     const dim3 mgrid(p.H, (p.B + sb - 1) / sb);
 #define MLRA_MERGE_CASE(xDC, xDH)                                                                       \
     if (DC == xDC && p.DH == xDH) {                                                                     \
-      if (sb == 4) hipLaunchKernelGGL((merge_mfma_kernel<xDC, xDH, 4>), mgrid, dim3(kMergeThreads), 0, stream, p); \
-      else if (sb == 2) hipLaunchKernelGGL((merge_mfma_kernel<xDC, xDH, 2>), mgrid, dim3(kMergeThreads), 0, stream, p); \
-      else hipLaunchKernelGGL((merge_mfma_kernel<xDC, xDH, 1>), mgrid, dim3(kMergeThreads), 0, stream, p); \
+      if (p.ws_o_f16) {                                                                                 \
+        if (sb == 4) hipLaunchKernelGGL((merge_mfma_kernel<xDC, xDH, 4, true>), mgrid, dim3(kMergeThreads), 0, stream, p); \
+        else if (sb == 2) hipLaunchKernelGGL((merge_mfma_kernel<xDC, xDH, 2, true>), mgrid, dim3(kMergeThreads), 0, stream, p); \
+        else hipLaunchKernelGGL((merge_mfma_kernel<xDC, xDH, 1, true>), mgrid, dim3(kMergeThreads), 0, stream, p); \
+      } else {                                                                                          \
+        if (sb == 4) hipLaunchKernelGGL((merge_mfma_kernel<xDC, xDH, 4, false>), mgrid, dim3(kMergeThreads), 0, stream, p); \
+        else if (sb == 2) hipLaunchKernelGGL((merge_mfma_kernel<xDC, xDH, 2, false>), mgrid, dim3(kMergeThreads), 0, stream, p); \
+        else hipLaunchKernelGGL((merge_mfma_kernel<xDC, xDH, 1, false>), mgrid, dim3(kMergeThreads), 0, stream, p); \
+      }                                                                                                 \
       return hipGetLastError();                                                                         \
     }
     MLRA_MERGE_CASE(32, 128)

@@ -261,7 +261,8 @@ mlra_status make_plan(const mlra_decode_args* a, bool check_pointers, const Topo
       mlra::merge_lds_bytes(a->num_branches, a->branch_dim, p.num_splits) > mlra::kMergeLdsLimit)
     return fail(MLRA_ERR_UNSUPPORTED, "%d splits x %d branches exceed the merge kernel's LDS", p.num_splits, a->num_branches);
   const size_t recs = (size_t)a->batch * p.num_splits * a->num_heads * a->num_branches;
-  p.ws_o_bytes = round_up(recs * a->branch_dim * sizeof(float), 256);
+  // fp16 output records where the MFMA kernel has several branches (see AttnParams), fp32 else
+  p.ws_o_bytes = round_up(recs * a->branch_dim * (p.mfma && a->num_branches > 1 ? 2 : 4), 256);
   p.ws_ml_bytes = round_up(recs * 2 * sizeof(float), 256);
   p.ws_bytes = p.ws_o_bytes + p.ws_ml_bytes;
   *plan = p;
@@ -370,7 +371,8 @@ mlra_status run_decode(const mlra_decode_args* a, void* stream_v) {
   p.q_scale = a->sm_scale * 1.4426950408889634f;
   p.split_tokens = plan.split_tokens;
   p.num_splits = plan.num_splits;
-  p.ws_o = static_cast<float*>(a->workspace);
+  p.ws_o = a->workspace;
+  p.ws_o_f16 = plan.mfma && a->num_branches > 1;
   p.ws_ml = reinterpret_cast<float*>(static_cast<char*>(a->workspace) + plan.ws_o_bytes);
   p.error_flags = a->error_flags;
 
@@ -389,6 +391,7 @@ mlra_status run_decode(const mlra_decode_args* a, void* stream_v) {
 
   mlra::MergeParams m{};
   m.ws_o = p.ws_o;
+  m.ws_o_f16 = p.ws_o_f16;
   m.ws_ml = p.ws_ml;
   m.seq_lens = a->seq_lens;
   m.w_v = a->w_v;

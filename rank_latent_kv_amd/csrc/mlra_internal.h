@@ -11,7 +11,10 @@ namespace mlra {
 
 // Partial softmax state written by the attention kernels, one record per
 // (sequence, split, head, branch):
-//   o  [B][S][H][NB][DB] fp32  unnormalised sum_s 2^(x_s - m) c_s
+//   o  [B][S][H][NB][DB] unnormalised sum_s 2^(x_s - m) c_s: fp32, or (ws_o_f16: the MFMA
+//                        kernel with several branches) fp16 scaled by 2^-e, where l = f 2^e
+//                        with f in [0.5, 1), and e added to m, so that (o, m, l) describe the
+//                        same softmax state and the records stay in fp16's range
 //   ml [B][S][H][NB][2]  fp32  (m, l): reference max in log2 units and sum 2^(x_s - m)
 // where x_s = z_s * log2(e) is the logit in log2 units.
 struct AttnParams {
@@ -31,13 +34,14 @@ struct AttnParams {
   float q_scale;           // sm_scale * log2(e)
   int32_t split_tokens;    // tokens per split (multiple of the kernel's stage)
   int32_t num_splits;      // splits of the longest sequence (record stride S)
-  float* ws_o;
+  void* ws_o;              // fp32, or fp16 scaled records (ws_o_f16)
   float* ws_ml;
   uint32_t* error_flags;
+  int32_t ws_o_f16;
 };
 
 struct MergeParams {
-  const float* ws_o;
+  const void* ws_o;
   const float* ws_ml;
   const int32_t* seq_lens;
   const void* w_v;         // [H][DH][NB*DB]
@@ -49,6 +53,7 @@ struct MergeParams {
   float alpha;
   int32_t w_dtype;         // mlra_dtype
   int32_t out_dtype;
+  int32_t ws_o_f16;
 };
 
 // MFMA (bf16) attention: kernel shapes compiled into the library.

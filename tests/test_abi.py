@@ -98,15 +98,30 @@ def test_valid_args_pass_validation():
 
 
 def test_workspace_size_formula():
+    """One record per (sequence, split, head, branch): d_b outputs (fp16 for the MFMA kernel with
+    several branches, as here) and an fp32 (m, l) pair, each array rounded up to 256 bytes."""
     a = base_args(B=16, L=32768)
     n = R.workspace_size(a)
     # MFMA path: 128-token stages, about one work-group per CU -> 16 splits of 2048 tokens
     recs = 16 * 16 * 64 * 4
-    expect = -(-recs * 32 * 4 // 256) * 256 + -(-recs * 2 * 4 // 256) * 256
+    expect = -(-recs * 32 * 2 // 256) * 256 + -(-recs * 2 * 4 // 256) * 256
     assert n == expect
     a.num_splits = 7
     n7 = R.workspace_size(a)
-    assert n7 == -(-16 * 7 * 64 * 4 * 32 * 4 // 256) * 256 + -(-16 * 7 * 64 * 4 * 2 * 4 // 256) * 256
+    assert n7 == -(-16 * 7 * 64 * 4 * 32 * 2 // 256) * 256 + -(-16 * 7 * 64 * 4 * 2 * 4 // 256) * 256
+
+
+def test_workspace_size_keeps_fp32_outputs_off_the_multi_branch_mfma_kernel():
+    """fp32 inputs (the generic kernel) and one-branch MFMA shapes keep fp32 output records."""
+    f = base_args(B=2, L=4096, dtype=R.MLRA_F32)
+    f.num_splits = 3
+    recs = 2 * 3 * 64 * 4
+    assert R.workspace_size(f) == -(-recs * 32 * 4 // 256) * 256 + -(-recs * 2 * 4 // 256) * 256
+    m = base_args(B=2, L=4096, NB=1, DB=128)   # MLA: the MFMA kernel with one 128-wide branch
+    m.num_splits = 3
+    recs = 2 * 3 * 64
+    assert R.plan(m, cu_count=256)["kernel"] == "mfma"
+    assert R.workspace_size(m) == -(-recs * 128 * 4 // 256) * 256 + -(-recs * 2 * 4 // 256) * 256
 
 
 @pytest.mark.parametrize("field,value,status", [
@@ -329,7 +344,7 @@ def test_split_limits_follow_the_merge_kernel():
     a = base_args(B=1, L=L)
     a.num_splits = 4096
     n = R.workspace_size(a)
-    assert n == 4096 * 64 * 4 * 32 * 4 + 4096 * 64 * 4 * 2 * 4
+    assert n == 4096 * 64 * 4 * 32 * 2 + 4096 * 64 * 4 * 2 * 4   # fp16 outputs, fp32 (m, l)
     a.num_splits = 4097          # rounds up to 128-token splits again: still 4096 of them
     assert R.workspace_size(a) == n
     f = base_args(B=1, L=L, dtype=R.MLRA_F32)
@@ -351,7 +366,7 @@ def test_auto_split_fits_one_pass_over_the_cus():
     a = base_args(B=4, L=max(lens), lens=lens)
     n = R.workspace_size(a)
     recs_per_split = 4 * 64 * 4
-    splits = n // (recs_per_split * 32 * 4 + recs_per_split * 2 * 4)
+    splits = n // (recs_per_split * 32 * 2 + recs_per_split * 2 * 4)   # fp16 outputs, fp32 (m, l)
     split_tokens = -(-max(lens) // splits)
     groups = sum(-(-L // (-(-split_tokens // 128) * 128)) for L in lens)
     assert splits == -(-max(lens) // 1792)
@@ -360,10 +375,11 @@ def test_auto_split_fits_one_pass_over_the_cus():
 
 def _auto_split_tokens(lens):
     """The automatic split of an MLRA-4 headline-shaped launch, read back from the workspace
-    size (one record of 32 fp32 outputs and an (m, l) pair per sequence, split, head, branch)."""
+    size (one record of 32 fp16 outputs and an fp32 (m, l) pair per sequence, split, head,
+    branch)."""
     a = base_args(B=len(lens), L=max(lens), lens=lens)
     recs_per_split = len(lens) * 64 * 4
-    splits = R.workspace_size(a) // (recs_per_split * 32 * 4 + recs_per_split * 2 * 4)
+    splits = R.workspace_size(a) // (recs_per_split * 32 * 2 + recs_per_split * 2 * 4)
     return splits, -(-max(lens) // splits)
 
 
@@ -432,7 +448,7 @@ def test_auto_split_one_long_context_among_many_short(n_short):
     t0 = time.perf_counter()
     n = R.workspace_size(a)
     dt = time.perf_counter() - t0
-    splits = n // (len(lens) * 64 * 4 * (32 * 4 + 2 * 4))
+    splits = n // (len(lens) * 64 * 4 * (32 * 2 + 2 * 4))
     assert splits == _planner_by_linear_scan(lens)
     if n_short == 1023:
         assert splits == 1
