@@ -16,6 +16,7 @@
 #include <hip/hip_bf16.h>
 
 #include <cmath>
+#include <type_traits>
 
 #include "mlra_internal.h"
 
@@ -169,39 +170,12 @@ __global__ __launch_bounds__(kMergeThreads) void merge_mfma_kernel(MergeParams p
   const bool active = part < PAR && beta < p.B;
   const int beta_c = beta < p.B ? beta : p.B - 1;
 
-  // loads of one round of kChunk splits (clamped to the last split; unused ones are discarded)
-  float mv[kChunk], lv[kChunk];
-  float4 ov[kChunk];
-  auto load_round = [&](int s0) __attribute__((always_inline)) {
-#pragma unroll
-    for (int j = 0; j < kChunk; ++j) {
-      const int sp = s0 + j * PAR;
-      const int spc = sp < S ? sp : S - 1;
-      const int64_t rec = (((int64_t)beta_c * S + spc) * p.H + head) * NB + b;
-      const float2 ml = *reinterpret_cast<const float2*>(p.ws_ml + rec * 2);
-      mv[j] = ml.x;
-      lv[j] = ml.y;
-      const int64_t oi = rec * DB + (k - b * DB);
-      if constexpr (F16) {
-        const uint2 w = *reinterpret_cast<const uint2*>(static_cast<const _Float16*>(p.ws_o) + oi);
-        ov[j] = make_float4((float)__builtin_bit_cast(_Float16, (unsigned short)(w.x & 0xffffu)),
-                            (float)__builtin_bit_cast(_Float16, (unsigned short)(w.x >> 16)),
-                            (float)__builtin_bit_cast(_Float16, (unsigned short)(w.y & 0xffffu)),
-                            (float)__builtin_bit_cast(_Float16, (unsigned short)(w.y >> 16)));
-      } else {
-        ov[j] = *reinterpret_cast<const float4*>(static_cast<const float*>(p.ws_o) + oi);
-      }
-    }
-  };
-  // Order of the requests: the sequence length and the first round of partials, then the
-  // W^V_i operands (needed last), so that one memory latency covers them all.
-  int ns = 0;
-  if (active) {
-    int L = p.seq_lens[beta];
-    L = L < 0 ? 0 : (L > p.max_seq_len ? p.max_seq_len : L);
-    ns = (L + p.split_tokens - 1) / p.split_tokens;
-    load_round(part);
-  }
+  // The W^V_i operands of this wave's output tiles go out first: every output tile is some
+  // wave's (d_h / 16 tiles over 4 waves), so the loads are unconditional and nothing waits
+  // between them. Then the sequence length and the first round of split records, kept raw
+  // (fp16 records are converted where the merge uses them), so that no conversion makes the
+  // wave wait for one load before it issues the next: one memory latency covers them all.
+  static_assert(NT % 4 == 0, "the 4 waves own every output tile");
   const __bf16* wv = reinterpret_cast<const __bf16*>(p.w_v) + (int64_t)head * DH * DC;
   bf16x8 wreg[NTW][KC];
 #pragma unroll
@@ -209,9 +183,42 @@ __global__ __launch_bounds__(kMergeThreads) void merge_mfma_kernel(MergeParams p
     const int nt = wave + 4 * t;
 #pragma unroll
     for (int kc = 0; kc < KC; ++kc)
-      wreg[t][kc] = nt < NT ? __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(
-                                  wv + (int64_t)(nt * 16 + r16) * DC + 32 * kc + 8 * kg))
-                            : bf16x8{};
+      wreg[t][kc] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(
+                        wv + (int64_t)(nt * 16 + r16) * DC + 32 * kc + 8 * kg));
+  }
+  // loads of one round of kChunk splits (clamped to the last split; unused ones are discarded)
+  float2 mlv[kChunk];
+  typedef typename std::conditional<F16, uint2, float4>::type Raw;
+  Raw ov[kChunk];
+  auto load_round = [&](int s0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < kChunk; ++j) {
+      const int sp = s0 + j * PAR;
+      const int spc = sp < S ? sp : S - 1;
+      const int64_t rec = (((int64_t)beta_c * S + spc) * p.H + head) * NB + b;
+      mlv[j] = *reinterpret_cast<const float2*>(p.ws_ml + rec * 2);
+      const int64_t oi = rec * DB + (k - b * DB);
+      if constexpr (F16) ov[j] = *reinterpret_cast<const uint2*>(static_cast<const _Float16*>(p.ws_o) + oi);
+      else ov[j] = *reinterpret_cast<const float4*>(static_cast<const float*>(p.ws_o) + oi);
+    }
+  };
+  auto value = [&](int j) __attribute__((always_inline)) -> float4 {
+    if constexpr (F16) {
+      const uint2 w = ov[j];
+      return make_float4((float)__builtin_bit_cast(_Float16, (unsigned short)(w.x & 0xffffu)),
+                         (float)__builtin_bit_cast(_Float16, (unsigned short)(w.x >> 16)),
+                         (float)__builtin_bit_cast(_Float16, (unsigned short)(w.y & 0xffffu)),
+                         (float)__builtin_bit_cast(_Float16, (unsigned short)(w.y >> 16)));
+    } else {
+      return ov[j];
+    }
+  };
+  int ns = 0;
+  if (active) {
+    int L = p.seq_lens[beta];
+    L = L < 0 ? 0 : (L > p.max_seq_len ? p.max_seq_len : L);
+    ns = (L + p.split_tokens - 1) / p.split_tokens;
+    load_round(part);
   }
   for (int i = tid; i < 16 * UROW; i += kMergeThreads) {
     (&uhi[0][0])[i] = (__bf16)0.f;
@@ -229,7 +236,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_mfma_kernel(MergeParams p
 #pragma unroll
         for (int j = 0; j < kChunk; ++j) {
           const bool ok = s0 + j * PAR < ns;
-          mc = ok ? fmaxf(mc, mv[j]) : mc;
+          mc = ok ? fmaxf(mc, mlv[j].x) : mc;
         }
         const float fold = (m_loc == -INFINITY) ? 0.f : exp2f(m_loc - mc);
         l_loc *= fold;
@@ -237,12 +244,13 @@ __global__ __launch_bounds__(kMergeThreads) void merge_mfma_kernel(MergeParams p
 #pragma unroll
         for (int j = 0; j < kChunk; ++j) {
           const bool ok = s0 + j * PAR < ns;
-          const float wj = ok ? exp2f(mv[j] - mc) : 0.f;
-          l_loc += ok ? wj * lv[j] : 0.f;
-          o_loc.x += ok ? wj * ov[j].x : 0.f;
-          o_loc.y += ok ? wj * ov[j].y : 0.f;
-          o_loc.z += ok ? wj * ov[j].z : 0.f;
-          o_loc.w += ok ? wj * ov[j].w : 0.f;
+          const float wj = ok ? exp2f(mlv[j].x - mc) : 0.f;
+          const float4 v = value(j);
+          l_loc += ok ? wj * mlv[j].y : 0.f;
+          o_loc.x += ok ? wj * v.x : 0.f;
+          o_loc.y += ok ? wj * v.y : 0.f;
+          o_loc.z += ok ? wj * v.z : 0.f;
+          o_loc.w += ok ? wj * v.w : 0.f;
         }
         m_loc = mc;
       }
@@ -278,26 +286,31 @@ __global__ __launch_bounds__(kMergeThreads) void merge_mfma_kernel(MergeParams p
   }
   __syncthreads();
 
-  // 3. Y = U . W^T on 16x16x32 MFMAs; each wave owns every 4th 16-column tile of d_h
+  // 3. Y = U . W^T on 16x16x32 MFMAs; each wave owns every 4th 16-column tile of d_h. The
+  //    tiles' chains run interleaved (each still in K order, hi before lo), over U operands
+  //    read from LDS once per K-chunk.
+  f32x4 acc[NTW];
+#pragma unroll
+  for (int t = 0; t < NTW; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kc = 0; kc < KC; ++kc) {
+    const bf16x8 ah = *reinterpret_cast<const bf16x8*>(&uhi[r16][32 * kc + 8 * kg]);
+    const bf16x8 al = *reinterpret_cast<const bf16x8*>(&ulo[r16][32 * kc + 8 * kg]);
+#pragma unroll
+    for (int t = 0; t < NTW; ++t) acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, wreg[t][kc], acc[t], 0, 0, 0);
+#pragma unroll
+    for (int t = 0; t < NTW; ++t) acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, wreg[t][kc], acc[t], 0, 0, 0);
+  }
 #pragma unroll
   for (int t = 0; t < NTW; ++t) {
     const int nt = wave + 4 * t;
-    if (nt >= NT) break;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kc = 0; kc < KC; ++kc) {
-      const bf16x8 ah = *reinterpret_cast<const bf16x8*>(&uhi[r16][32 * kc + 8 * kg]);
-      const bf16x8 al = *reinterpret_cast<const bf16x8*>(&ulo[r16][32 * kc + 8 * kg]);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, wreg[t][kc], acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, wreg[t][kc], acc, 0, 0, 0);
-    }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int bo = 4 * kg + j;
       const int bt = beta0 + bo;
       if (bo >= SEQB || bt >= p.B) continue;
       const int64_t o = ((int64_t)bt * p.H + head) * DH + nt * 16 + r16;
-      const float yv = acc[j] * p.alpha;
+      const float yv = acc[t][j] * p.alpha;
       if (p.out_dtype == 0) reinterpret_cast<__hip_bfloat16*>(p.out)[o] = __float2bfloat16(yv);
       else reinterpret_cast<float*>(p.out)[o] = yv;
     }
