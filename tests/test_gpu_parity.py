@@ -110,6 +110,21 @@ def test_generic_bf16_shape():
     check(w, make_inputs(w, seq_lens=[300, 700]))
 
 
+@pytest.mark.parametrize("nb,db,dh", [(4, 32, 64), (4, 32, 256), (8, 32, 128), (2, 32, 128)])
+def test_mfma_merge_shapes(nb, db, dh):
+    """Every MFMA merge build beyond the workloads' own (d_c, d_h): (128, 64), (128, 256),
+    (256, 128) and (64, 128). Eight heads have no attention build, so the generic attention
+    kernel writes the fp32 split records and the MFMA merge (W^V operands requested before the
+    records, one 16-wide output tile per wave and tile slot) applies W^V; several splits per
+    sequence exercise its log-sum-exp merge."""
+    w = PRESETS["mlra4_b16_l32k"].replace(batch=3, heads=8, branches=nb, branch_dim=db, head_dim=dh,
+                                           name=f"merge_dc{nb * db}_dh{dh}")
+    inp = make_inputs(w, seq_lens=[1300, 520, 77])
+    say(f"mfma merge d_c={nb * db} d_h={dh}")
+    for ns in (0, 5):
+        check(w, inp, num_splits=ns)
+
+
 @pytest.mark.parametrize("preset,mla", [("mlra4_b16_l32k", False), ("mla_b16_l32k", True),
                                         ("mlra4_tp_shard_b64_l64k", False), ("mla_tp_shard_b64_l64k", True),
                                         ("mlra2_b16_l32k", False)])
