@@ -120,6 +120,10 @@ struct Cfg {
   static constexpr int NS = NS_FIT < kMaxStages ? NS_FIT : kMaxStages;   // ring depth
   static constexpr int RING_BYTES = NS * STAGE_BYTES;
   static constexpr bool PIPE2 = BPW > 1 && W <= 8 && NS >= 4;
+  // fp16 split records where the phase merge leaves each wave whole 4-row groups (two phases
+  // with several branches, four with one); with eight phases a wave writes 2-row pieces, which
+  // as fp16 would be 4-byte stores, and keeps fp32 records
+  static constexpr bool F16REC = P == 2 || P == 4;
   static constexpr int MERGE_BYTES = MERGE_WAVES * MERGE_FLOATS * 4;
   static constexpr int LDS_BYTES = (RING_BYTES > MERGE_BYTES ? RING_BYTES : MERGE_BYTES) + PTAB_BYTES;
   static_assert(NB % BPW == 0, "branches per wave must divide the branches");
@@ -987,6 +991,39 @@ __global__ __launch_bounds__(W * 64, 1) void attn_mfma_kernel(AttnParams p) {
         }
       }
       return;
+    } else if constexpr (C::F16REC) {
+      // One branch over four phases: the phase owns the 4-row group qa = r0 / 4 of every
+      // output tile, 4 consecutive features per lane (8 bytes of fp16; lanes l and l + 32 of a
+      // head cover 16 contiguous bytes), scaled per record as above. Ordinary stores.
+      static_assert(C::P == 4, "one-branch fp16 records: each phase owns one 4-row group");
+      typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+      auto pk = [&](float a, float b) __attribute__((always_inline)) {
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, f16x2));
+      };
+      const int qa = r0 / 4;
+#pragma unroll
+      for (int h = 0; h < C::HPW; ++h) {
+        const int head = (hgslot * C::HPW + h) * 32 + n32;
+        if (head >= p.H) continue;
+#pragma unroll
+        for (int bb = 0; bb < BPW; ++bb) {
+          const int64_t rec = (((int64_t)beta * p.num_splits + split) * p.H + head) * NB + bg * BPW + bb;
+          const float l = lsum[h][bb];
+          const int e = (int)((__float_as_uint(l) >> 23) & 0xff) - 126;
+          const float sc = __uint_as_float((uint32_t)(127 - e) << 23);
+          _Float16* o16 = static_cast<_Float16*>(p.ws_o) + rec * DB;
+#pragma unroll
+          for (int mt = 0; mt < C::MT; ++mt) {
+            const f32x16& v = acc[h][bb][mt];
+            const int q = 4 * qa;
+            *reinterpret_cast<uint2*>(o16 + 32 * mt + 8 * qa + 4 * g) =
+                make_uint2(pk(v[q] * sc, v[q + 1] * sc), pk(v[q + 2] * sc, v[q + 3] * sc));
+          }
+          if (ml && g == 0)
+            *reinterpret_cast<float2*>(p.ws_ml + rec * 2) = make_float2(mref[h][bb] + (float)e, l * sc);
+        }
+      }
+      return;
     }
 #pragma unroll
     for (int h = 0; h < C::HPW; ++h) {
@@ -1138,6 +1175,14 @@ int mfma_min_page_size(int nb, int db, int dr, int heads) {
   MLRA_MFMA_SHAPES(X)
 #undef X
   return 1;
+}
+
+bool mfma_f16_records(int nb, int db, int dr, int heads) {
+#define X(xNB, xDB, xDR, xH, xW, xBPW) \
+  if (nb == xNB && db == xDB && dr == xDR && heads == xH) return Cfg<xNB, xDB, xDR, xH, xW, false, xBPW>::F16REC;
+  MLRA_MFMA_SHAPES(X)
+#undef X
+  return false;
 }
 
 int mfma_stage_tokens(int nb, int db, int dr, int heads) {

@@ -72,6 +72,7 @@ struct Plan {
   size_t ws_o_bytes = 0;
   size_t ws_ml_bytes = 0;
   size_t ws_bytes = 0;
+  bool f16_records = false;   // the attention kernel writes fp16 split records
 };
 
 int64_t total_tokens_estimate(const mlra_decode_args* a) {
@@ -261,8 +262,9 @@ mlra_status make_plan(const mlra_decode_args* a, bool check_pointers, const Topo
       mlra::merge_lds_bytes(a->num_branches, a->branch_dim, p.num_splits) > mlra::kMergeLdsLimit)
     return fail(MLRA_ERR_UNSUPPORTED, "%d splits x %d branches exceed the merge kernel's LDS", p.num_splits, a->num_branches);
   const size_t recs = (size_t)a->batch * p.num_splits * a->num_heads * a->num_branches;
-  // fp16 output records where the MFMA kernel has several branches (see AttnParams), fp32 else
-  p.ws_o_bytes = round_up(recs * a->branch_dim * (p.mfma && a->num_branches > 1 ? 2 : 4), 256);
+  // fp16 output records where the MFMA kernel writes them (see AttnParams), fp32 else
+  p.f16_records = p.mfma && mlra::mfma_f16_records(a->num_branches, a->branch_dim, a->rope_dim, a->num_heads);
+  p.ws_o_bytes = round_up(recs * a->branch_dim * (p.f16_records ? 2 : 4), 256);
   p.ws_ml_bytes = round_up(recs * 2 * sizeof(float), 256);
   p.ws_bytes = p.ws_o_bytes + p.ws_ml_bytes;
   *plan = p;
@@ -372,7 +374,7 @@ mlra_status run_decode(const mlra_decode_args* a, void* stream_v) {
   p.split_tokens = plan.split_tokens;
   p.num_splits = plan.num_splits;
   p.ws_o = a->workspace;
-  p.ws_o_f16 = plan.mfma && a->num_branches > 1;
+  p.ws_o_f16 = plan.f16_records;
   p.ws_ml = reinterpret_cast<float*>(static_cast<char*>(a->workspace) + plan.ws_o_bytes);
   p.error_flags = a->error_flags;
 

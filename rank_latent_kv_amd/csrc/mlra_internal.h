@@ -12,7 +12,7 @@ namespace mlra {
 // Partial softmax state written by the attention kernels, one record per
 // (sequence, split, head, branch):
 //   o  [B][S][H][NB][DB] unnormalised sum_s 2^(x_s - m) c_s: fp32, or (ws_o_f16: the MFMA
-//                        kernel with several branches) fp16 scaled by 2^-e, where l = f 2^e
+//                        shapes of mfma_f16_records) fp16 scaled by 2^-e, where l = f 2^e
 //                        with f in [0.5, 1), and e added to m, so that (o, m, l) describe the
 //                        same softmax state and the records stay in fp16's range
 //   ml [B][S][H][NB][2]  fp32  (m, l): reference max in log2 units and sum 2^(x_s - m)
@@ -62,6 +62,8 @@ struct MfmaShape {
 };
 // Stage size in tokens of the MFMA kernel for this shape (0 if not built).
 int mfma_stage_tokens(int nb, int db, int dr, int heads);
+// Whether the MFMA kernel of this shape writes fp16 split records (else fp32).
+bool mfma_f16_records(int nb, int db, int dr, int heads);
 // Pages one split of the paged MFMA kernel of this shape may span.
 int mfma_page_cache(int nb, int db, int dr, int heads);
 // Smallest page size (tokens) the paged MFMA kernel of this shape takes.

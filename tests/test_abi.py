@@ -111,17 +111,21 @@ def test_workspace_size_formula():
     assert n7 == -(-16 * 7 * 64 * 4 * 32 * 2 // 256) * 256 + -(-16 * 7 * 64 * 4 * 2 * 4 // 256) * 256
 
 
-def test_workspace_size_keeps_fp32_outputs_off_the_multi_branch_mfma_kernel():
-    """fp32 inputs (the generic kernel) and one-branch MFMA shapes keep fp32 output records."""
+def test_workspace_size_keeps_fp32_outputs_where_the_kernel_writes_them():
+    """fp32 inputs (the generic kernel) and the MFMA shape whose waves write 2-row pieces (the
+    16-head one-branch shard of eight phases) keep fp32 output records; the one-branch shapes
+    of four phases (MLA at 64 heads, the 16-head MLA shard, the 64-head branch shard) write
+    fp16 ones, like the multi-branch shapes."""
     f = base_args(B=2, L=4096, dtype=R.MLRA_F32)
     f.num_splits = 3
     recs = 2 * 3 * 64 * 4
     assert R.workspace_size(f) == -(-recs * 32 * 4 // 256) * 256 + -(-recs * 2 * 4 // 256) * 256
-    m = base_args(B=2, L=4096, NB=1, DB=128)   # MLA: the MFMA kernel with one 128-wide branch
-    m.num_splits = 3
-    recs = 2 * 3 * 64
-    assert R.plan(m, cu_count=256)["kernel"] == "mfma"
-    assert R.workspace_size(m) == -(-recs * 128 * 4 // 256) * 256 + -(-recs * 2 * 4 // 256) * 256
+    for nb, db, h, eb in ((1, 128, 64, 2), (1, 128, 16, 2), (1, 32, 64, 2), (1, 32, 16, 4)):
+        m = base_args(B=2, L=4096, NB=nb, DB=db, H=h)
+        m.num_splits = 3
+        recs = 2 * 3 * h * nb
+        assert R.plan(m, cu_count=256)["kernel"] == "mfma"
+        assert R.workspace_size(m) == -(-recs * db * eb // 256) * 256 + -(-recs * 2 * 4 // 256) * 256, (nb, db, h)
 
 
 @pytest.mark.parametrize("field,value,status", [

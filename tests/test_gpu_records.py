@@ -1,6 +1,7 @@
 """The attention kernel's split records, read back from the workspace (a white-box check).
 
-With several branches the kernel stores each split's unnormalised output o in fp16, scaled
+With several branches, or one branch over four phases (MLA), the kernel stores each split's
+unnormalised output o in fp16, scaled
 by 2^-e where l = f 2^e with f in [0.5, 1), and adds e to m: every record it writes must then
 hold l in [0.5, 1), a finite m, and |o| <= l * max|c| (o is an l-weighted mean of cache
 values). The workspace starts as NaN bytes, so a record left unwritten, or written with
@@ -17,7 +18,7 @@ from gpu_helpers import DEV, f64, oracle_decode, row_rel_err, say, to_dev
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("preset", ["mlra4_b16_l32k", "mlra2_b16_l32k"])
+@pytest.mark.parametrize("preset", ["mlra4_b16_l32k", "mlra2_b16_l32k", "mla_b16_l32k"])
 def test_every_fp16_record_is_a_finite_in_range_softmax_state(preset):
     w = PRESETS[preset]
     inp = make_inputs(w)
@@ -32,7 +33,8 @@ def test_every_fp16_record_is_a_finite_in_range_softmax_state(preset):
     n = R.workspace_size(args)
     ws = torch.full((n,), 0xFF, dtype=torch.uint8, device=DEV)   # NaN in fp16 and fp32
     say(f"records of {preset}, {plan['num_splits']} splits")
-    y = R.decode(d["q_lat"], d["q_rope"], kv[..., :dc], kv[..., dc:], d["seq_lens"], d["w_v"], workspace=ws, **kw)
+    fn = R.mla_decode if w.branches == 1 else R.decode
+    y = fn(d["q_lat"], d["q_rope"], kv[..., :dc], kv[..., dc:], d["seq_lens"], d["w_v"], workspace=ws, **kw)
     torch.cuda.synchronize()
 
     B, S, H, NB, DB = w.batch, plan["num_splits"], w.heads, w.branches, w.branch_dim
